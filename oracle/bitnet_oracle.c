@@ -1,0 +1,262 @@
+/*
+ * bitnet_oracle.c -- plain, slow CPU oracle for the BitNet b1.58 W2A8 (I2_S)
+ * matmul.  TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and
+ * the benchmark's CPU-baseline leg, never by the library.  No SIMD
+ * intrinsics, no blocking, no code shared with the GPU path.  Page keys
+ * [P1]..[P4] are listed in bitnet_oracle.h.
+ *
+ * Built with: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * (no FMA contraction: every float operation below is a single IEEE-754
+ * binary32 or binary64 operation, as written).
+ */
+#define _POSIX_C_SOURCE 200809L
+#include "bitnet_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Block size of the I2_S layout on the x86 path [P1 §4-2]; the packed files
+ * the pages work with always use 128 [P2 §3]. */
+#define ORC_QK 128
+
+int orc_code_of_weight(int w)
+{
+    /* [P1 §1-1] table: -1 -> 0 (bits 00), 0 -> 1 (01), +1 -> 2 (10). */
+    if (w == -1) return 0;
+    if (w == 0) return 1;
+    if (w == 1) return 2;
+    return -1;
+}
+
+int orc_weight_of_code(int c)
+{
+    /* Inverse of the same table; the worked byte of [P1 §8] takes c - 1. */
+    if (c >= 0 && c <= 2) return c - 1;
+    return 99;
+}
+
+int64_t orc_pack_i2s(const int8_t *w, int64_t M, int64_t K, uint8_t *packed)
+{
+    /* [P1 §4-2]: a block holds 128 consecutive weights of a row in 32 bytes.
+     * Position p of the block (0..127) is stored in byte (p mod 32) of the
+     * block, in the 2-bit field that starts at bit 6 - 2*(p div 32): the four
+     * weights p, p+32, p+64, p+96 share one byte, the first in the top bits.
+     * Blocks follow each other along the row and rows are contiguous, so the
+     * block of weight (m, k) starts at byte m*K/4 + 32*(k div 128). */
+    int64_t nonternary = 0;
+    memset(packed, 0, (size_t)(M * K / 4));
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) {
+            int c = orc_code_of_weight(w[m * K + k]);
+            if (c < 0) {           /* not ternary: mark the slot with code 3 */
+                nonternary++;
+                c = 3;
+            }
+            int64_t blk = k / ORC_QK;
+            int64_t p = k % ORC_QK;
+            int64_t at = m * (K / 4) + blk * 32 + p % 32;
+            int bit = 6 - 2 * (int)(p / 32);
+            packed[at] = (uint8_t)(packed[at] | (c << bit));
+        }
+    }
+    return nonternary;
+}
+
+int64_t orc_unpack_i2s(const uint8_t *packed, int64_t M, int64_t K, int8_t *w)
+{
+    /* For weight (m, k): block b = k / 128 of row m starts at byte
+     * m*(K/4) + 32*b [P2 §3: row offset, 32 bytes per block]; inside the
+     * block, position p = k % 128 lives in byte p % 32 at bits
+     * (6 - 2*(p/32)) .. +1, i.e. group 0 in bits 7-6 [P1 §8; P3 §4]. */
+    int64_t bad = 0;
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) {
+            int64_t b = k / ORC_QK;
+            int64_t p = k % ORC_QK;
+            uint8_t byte = packed[m * (K / 4) + 32 * b + (p % 32)];
+            int shift = 6 - 2 * (int)(p / 32);
+            int code = (byte >> shift) & 3;
+            int wv = orc_weight_of_code(code);
+            if (wv == 99) bad++;
+            w[m * K + k] = (int8_t)wv;
+        }
+    }
+    return bad;
+}
+
+float orc_bf16_to_f32(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+static void quant_row(const float *x, int64_t K, int8_t *q, float *s_out,
+                      int32_t *qsum_out)
+{
+    /* [P1 §4-5]: s = 127 / max(max|x|, 1e-5); q = round(x*s), clamped to the
+     * int8 range [P4: clip to [-128, 127]], stored as int8.  Round is IEEE
+     * round-half-to-even (rintf in the default rounding mode). */
+    float a = 0.0f;
+    for (int64_t k = 0; k < K; k++) {
+        float v = fabsf(x[k]);
+        if (v > a) a = v;
+    }
+    float denom = a > 1e-5f ? a : 1e-5f;
+    float s = 127.0f / denom;
+    int32_t sum = 0;
+    for (int64_t k = 0; k < K; k++) {
+        float t = x[k] * s;
+        float r = rintf(t);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -128.0f) r = -128.0f;
+        q[k] = (int8_t)r;
+        sum += (int32_t)q[k];
+    }
+    *s_out = s;
+    *qsum_out = sum;
+}
+
+void orc_quant_act_f32(const float *x, int64_t N, int64_t K, int8_t *q,
+                       float *s, int32_t *qsum)
+{
+    for (int64_t n = 0; n < N; n++)
+        quant_row(x + n * K, K, q + n * K, s + n, qsum + n);
+}
+
+void orc_quant_act_bf16(const uint16_t *x, int64_t N, int64_t K, int8_t *q,
+                        float *s, int32_t *qsum)
+{
+    float *row = (float *)malloc((size_t)K * sizeof(float));
+    if (!row) return;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) row[k] = orc_bf16_to_f32(x[n * K + k]);
+        quant_row(row, K, q + n * K, s + n, qsum + n);
+    }
+    free(row);
+}
+
+void orc_dot_def(const int8_t *w, const int8_t *q, int64_t M, int64_t K,
+                 int64_t N, int64_t *D)
+{
+    /* D = W_q @ x_q, an integer dot with no float multiply [P1 §1-1; P4]. */
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t m = 0; m < M; m++) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; k++)
+                acc += (int64_t)w[m * K + k] * (int64_t)q[n * K + k];
+            D[n * M + m] = acc;
+        }
+    }
+}
+
+void orc_dot_raw(const uint8_t *packed, const int8_t *q, const int32_t *qsum,
+                 int64_t M, int64_t K, int64_t N, int64_t *R, int64_t *D)
+{
+    /* [P2 §3; P3 §3.1-§4]: the packed row is read one byte at a time.  Byte t
+     * of the row belongs to block t div 32; its four 2-bit fields, taken from
+     * the top bits down, pair with the activations 0, 32, 64 and 96 places
+     * after (block start + t mod 32).  The raw codes 0/1/2 are what gets
+     * multiplied [P3 §3.2], so the sum over the row is
+     * R = sum((w+1)*x) = sum(w*x) + sum(x), and the exact dot is
+     * D = R - sum(x)  (the zero-mean shortcut of [P3 §3.2] is not taken). */
+    int64_t bytes_per_row = K / 4;
+    for (int64_t n = 0; n < N; n++) {
+        const int8_t *act = q + n * K;
+        for (int64_t m = 0; m < M; m++) {
+            const uint8_t *rowbytes = packed + m * bytes_per_row;
+            int64_t raw = 0;
+            for (int64_t t = 0; t < bytes_per_row; t++) {
+                int64_t base = (t / 32) * ORC_QK + (t % 32);
+                for (int field = 0; field < 4; field++) {
+                    int code = (rowbytes[t] >> (6 - 2 * field)) & 3;
+                    raw += (int64_t)code * (int64_t)act[base + 32 * field];
+                }
+            }
+            R[n * M + m] = raw;
+            D[n * M + m] = raw - (int64_t)qsum[n];
+        }
+    }
+}
+
+void orc_epilogue(const int64_t *D, double alpha, const float *s, int64_t M,
+                  int64_t N, double *y)
+{
+    /* The integer dot leaves the scales to the caller [P2 §3]; the weight is
+     * q*alpha [P1 §6-2] and the activation is q/s [P1 §4-5], so the output is
+     * D * alpha / s. */
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t m = 0; m < M; m++)
+            y[n * M + m] = (double)D[n * M + m] * alpha / (double)s[n];
+}
+
+/* ---- threaded driver over output rows ---------------------------------- */
+
+typedef struct {
+    const uint8_t *packed;
+    int64_t M, K, N;
+    const int8_t *q;
+    const float *s;
+    double alpha;
+    int64_t r0, r1;
+    int64_t *D;
+    double *y;
+    int64_t bad;
+} orc_job;
+
+static void *linear_worker(void *arg)
+{
+    orc_job *j = (orc_job *)arg;
+    int8_t *wrow = (int8_t *)malloc((size_t)j->K);
+    if (!wrow) return NULL;
+    for (int64_t m = j->r0; m < j->r1; m++) {
+        /* unpack row m weight by weight (same addressing as orc_unpack_i2s) */
+        for (int64_t k = 0; k < j->K; k++) {
+            int64_t b = k / ORC_QK, p = k % ORC_QK;
+            uint8_t byte = j->packed[m * (j->K / 4) + 32 * b + (p % 32)];
+            int wv = orc_weight_of_code((byte >> (6 - 2 * (int)(p / 32))) & 3);
+            if (wv == 99) { j->bad++; wv = 0; }
+            wrow[k] = (int8_t)wv;
+        }
+        for (int64_t n = 0; n < j->N; n++) {
+            int64_t acc = 0;
+            const int8_t *qn = j->q + n * j->K;
+            for (int64_t k = 0; k < j->K; k++)
+                acc += (int64_t)wrow[k] * (int64_t)qn[k];
+            if (j->D) j->D[n * j->M + m] = acc;
+            if (j->y) j->y[n * j->M + m] = (double)acc * j->alpha / (double)j->s[n];
+        }
+    }
+    free(wrow);
+    return NULL;
+}
+
+int64_t orc_linear_i2s(const uint8_t *packed, int64_t M, int64_t K,
+                       const int8_t *q, int64_t N, const float *s, float alpha,
+                       int64_t row0, int64_t nrows, int64_t *D, double *y,
+                       int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nrows < nthreads) nthreads = nrows > 0 ? (int)nrows : 1;
+    orc_job jobs[256];
+    pthread_t tids[256];
+    int64_t per = nrows / nthreads, rem = nrows % nthreads, r = row0;
+    for (int t = 0; t < nthreads; t++) {
+        int64_t cnt = per + (t < rem ? 1 : 0);
+        jobs[t] = (orc_job){packed, M, K, N, q, s, (double)alpha, r, r + cnt, D, y, 0};
+        r += cnt;
+    }
+    for (int t = 1; t < nthreads; t++)
+        pthread_create(&tids[t], NULL, linear_worker, &jobs[t]);
+    linear_worker(&jobs[0]);
+    int64_t bad = jobs[0].bad;
+    for (int t = 1; t < nthreads; t++) {
+        pthread_join(tids[t], NULL);
+        bad += jobs[t].bad;
+    }
+    return bad;
+}

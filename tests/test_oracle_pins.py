@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test ties an oracle function to something the pages print (fixtures in
+tests/golden/, each carrying its citation), a closed form, an invariant of
+the mathematics, or brute force on tiny inputs.  The set is chosen so that a
+dropped term, a wrong sign, a wrong shift or index, or a transposed operand in
+the oracle fails at least one test.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from ternary_weight_i2_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fixture(name):
+    rows, kv = [], {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = [int(t) for t in v.split()]
+            else:
+                rows.append([t for t in line.split()])
+    return rows, kv
+
+
+# ---------------------------------------------------------------- code map
+def test_code_map_matches_page_table(orc):
+    rows, _ = _fixture("p1_code_map.txt")
+    assert len(rows) == 3
+    for w, code, bits in rows:
+        assert orc.code_of_weight(int(w)) == int(code)
+        assert format(int(code), "02b") == bits
+        assert orc.weight_of_code(int(code)) == int(w)
+    # no other weight has a code, and code 3 has no weight
+    for w in (-3, -2, 2, 3, 127, -128):
+        assert orc.code_of_weight(w) == -1
+    assert orc.weight_of_code(3) == 99
+
+
+# ------------------------------------------------------- worked byte (P1 §8)
+def test_worked_byte_pack(orc):
+    _, kv = _fixture("p1_worked_byte.txt")
+    w_top_first = kv["weights_top_first"]
+    # the four weights that share byte 0 of a block are elements 0/32/64/96
+    W = np.full((1, 128), 0, dtype=np.int8)
+    for g, wv in enumerate(w_top_first):
+        W[0, 32 * g] = wv
+    P, bad = orc.pack_i2s(W)
+    assert bad == 0
+    assert int(P[0, 0]) == kv["byte"][0]
+    # every other byte holds four zero weights = four codes 1 = 0b01010101
+    assert all(int(b) == 0x55 for b in P[0, 1:])
+
+
+def test_worked_byte_unpack(orc):
+    _, kv = _fixture("p1_worked_byte.txt")
+    P = np.full((1, 32), 0x55, dtype=np.uint8)
+    P[0, 0] = kv["byte"][0]
+    W, bad = orc.unpack_i2s(P, 128)
+    assert bad == 0
+    assert [int(W[0, 32 * g]) for g in range(4)] == kv["weights_top_first"]
+    codes = [orc.code_of_weight(int(W[0, 32 * g])) for g in range(4)]
+    assert codes == kv["codes_top_first"]
+
+
+# ------------------------------------------------------ interleave (P1 §4-2)
+def test_interleave_positions(orc):
+    rows, _ = _fixture("p1_interleave.txt")
+    for row in rows:
+        byte_idx = int(row[0])
+        elems = [int(t) for t in row[1:]]
+        for slot, e in enumerate(elems):
+            # one +1 (code 2) among -1s (code 0): exactly one non-zero byte
+            W = np.full((1, 128), -1, dtype=np.int8)
+            W[0, e] = 1
+            P, _ = orc.pack_i2s(W)
+            nz = np.nonzero(P[0])[0].tolist()
+            assert nz == [byte_idx]
+            # first listed element sits in the top two bits
+            assert int(P[0, byte_idx]) == 2 << (6 - 2 * slot)
+
+
+def test_blocks_and_rows_are_contiguous(orc):
+    # A +1 at (m, k) with -1 elsewhere lights exactly one byte; its index must
+    # grow by 32 per 128-block along k and by K/4 per row (rows back to back).
+    M, K = 3, 384
+    seen = []
+    for m in range(M):
+        for k in (0, 127, 128, 200, 383):
+            W = np.full((M, K), -1, dtype=np.int8)
+            W[m, k] = 1
+            P, _ = orc.pack_i2s(W)
+            nz = np.flatnonzero(P)
+            assert len(nz) == 1
+            seen.append((m, k, int(nz[0])))
+    byte = {(m, k): b for m, k, b in seen}
+    for m in range(M):
+        assert byte[(m, 128)] - byte[(m, 0)] == 32
+        assert byte[(m, 383)] - byte[(m, 0)] == 2 * 32 + 31
+    for k in (0, 127, 128, 200, 383):
+        assert byte[(1, k)] - byte[(0, k)] == K // 4
+        assert byte[(2, k)] - byte[(1, k)] == K // 4
+
+
+# -------------------------------------------------------- round trips
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 256), (17, 640), (64, 384)])
+def test_pack_unpack_roundtrip(orc, M, K):
+    rng = np.random.default_rng(M * 1000 + K)
+    for dist in ("uniform", "half_zero"):
+        W = synth.ternary(rng, M, K, dist)
+        P, bad = orc.pack_i2s(W)
+        assert bad == 0 and P.shape == (M, K // 4)
+        W2, bad2 = orc.unpack_i2s(P, K)
+        assert bad2 == 0
+        np.testing.assert_array_equal(W, W2)
+
+
+def test_all_valid_bytes_roundtrip(orc):
+    # 3^4 = 81 bytes hold four valid codes; unpack then pack restores each.
+    valid = [(a << 6) | (b << 4) | (c << 2) | d
+             for a in range(3) for b in range(3) for c in range(3) for d in range(3)]
+    assert len(valid) == 81
+    P = np.full((81, 32), 0x55, dtype=np.uint8)
+    for i, v in enumerate(valid):
+        P[i, i % 32] = v
+    W, bad = orc.unpack_i2s(P, 128)
+    assert bad == 0
+    P2, bad2 = orc.pack_i2s(W)
+    assert bad2 == 0
+    np.testing.assert_array_equal(P, P2)
+
+
+def test_nonternary_and_code3_detected(orc):
+    W = np.zeros((2, 128), dtype=np.int8)
+    W[1, 77] = 2
+    W[0, 3] = -5
+    P, bad = orc.pack_i2s(W)
+    assert bad == 2
+    _, bad_codes = orc.unpack_i2s(P, 128)
+    assert bad_codes == 2
+
+
+# ---------------------------------------------------- worked dot (P1 §1-1)
+def test_worked_dot_definition(orc):
+    _, kv = _fixture("p1_worked_dot.txt")
+    x = np.zeros((1, 128), dtype=np.int8)
+    w = np.zeros((1, 128), dtype=np.int8)
+    x[0, :4] = kv["x"]
+    w[0, :4] = kv["w"]
+    assert int(orc.dot_def(w, x)[0, 0]) == kv["dot"][0]
+
+
+def test_worked_dot_raw_code_identity(orc):
+    # sum(code*x) = sum(w*x) + sum(x): with the page's numbers 25 = 7 + 18.
+    _, kv = _fixture("p1_worked_dot.txt")
+    x = np.zeros((1, 128), dtype=np.int8)
+    w = np.zeros((1, 128), dtype=np.int8)
+    x[0, :4] = kv["x"]
+    w[0, :4] = kv["w"]
+    P, _ = orc.pack_i2s(w)
+    qsum = np.array([sum(kv["x"])], dtype=np.int32)
+    R, D = orc.dot_raw(P, x, qsum, 128)
+    assert int(D[0, 0]) == kv["dot"][0]
+    assert int(R[0, 0]) == kv["dot"][0] + sum(kv["x"]) == 25
+
+
+# ------------------------------------------------------- brute force
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (7, 256, 3), (64, 384, 8), (33, 128, 5)])
+def test_dot_def_vs_numpy_int64_matmul(orc, M, K, N):
+    rng = np.random.default_rng(7 * M + K + N)
+    W = synth.ternary(rng, M, K)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    ref = q.astype(np.int64) @ W.astype(np.int64).T
+    np.testing.assert_array_equal(orc.dot_def(W, q), ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 128, 1), (16, 512, 4), (9, 1152, 2)])
+def test_dot_raw_equals_definition(orc, M, K, N):
+    rng = np.random.default_rng(M + 11 * K + N)
+    for dist in ("uniform", "half_zero"):
+        W = synth.ternary(rng, M, K, dist)
+        q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+        qsum = q.astype(np.int64).sum(1).astype(np.int32)
+        P, _ = orc.pack_i2s(W)
+        R, D = orc.dot_raw(P, q, qsum, K)
+        Dd = orc.dot_def(W, q)
+        np.testing.assert_array_equal(D, Dd)
+        np.testing.assert_array_equal(R, Dd + qsum[:, None])
+
+
+# ------------------------------------------------------- closed forms
+def test_closed_forms(orc):
+    rng = np.random.default_rng(99)
+    M, K, N = 6, 256, 3
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    qsum = q.astype(np.int64).sum(1)
+    for fill, expect in ((0, 0 * qsum), (1, qsum), (-1, -qsum)):
+        W = np.full((M, K), fill, dtype=np.int8)
+        D = orc.dot_def(W, q)
+        assert (D == expect[:, None]).all()
+        P, _ = orc.pack_i2s(W)
+        R, D2 = orc.dot_raw(P, q, qsum.astype(np.int32), K)
+        np.testing.assert_array_equal(D2, D)
+        if fill == 0:
+            assert (R == qsum[:, None]).all()
+    # one-hot token picks a column of W
+    W = synth.ternary(rng, M, K)
+    for k in (0, 31, 32, 127, 128, 255):
+        e = np.zeros((1, K), dtype=np.int8)
+        e[0, k] = 1
+        np.testing.assert_array_equal(orc.dot_def(W, e)[0], W[:, k].astype(np.int64))
+        e[0, k] = -3
+        np.testing.assert_array_equal(orc.dot_def(W, e)[0], -3 * W[:, k].astype(np.int64))
+    # duplicated token rows give identical outputs
+    qq = np.concatenate([q[:1], q[:1]])
+    D = orc.dot_def(W, qq)
+    np.testing.assert_array_equal(D[0], D[1])
+
+
+# ------------------------------------------------------- quantisation
+def test_quant_absmax_maps_to_127(orc):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 512), dtype=np.float32)
+    q, s, qs = orc.quant_act(x)
+    for n in range(4):
+        k = int(np.argmax(np.abs(x[n])))
+        assert int(q[n, k]) == (127 if x[n, k] > 0 else -127)
+        assert np.abs(q[n]).max() == 127
+        assert int(qs[n]) == int(q[n].astype(np.int64).sum())
+
+
+def test_quant_constant_and_zero_rows(orc):
+    x = np.zeros((3, 256), dtype=np.float32)
+    x[0, :] = 0.37
+    x[1, :] = -2.5
+    q, s, qs = orc.quant_act(x)
+    assert (q[0] == 127).all() and int(qs[0]) == 127 * 256
+    assert (q[1] == -127).all() and int(qs[1]) == -127 * 256
+    # all-zero token: floor 1e-5 (fp32) -> s ~ 1.27e7, q = 0, sum 0
+    assert (q[2] == 0).all() and int(qs[2]) == 0
+    assert abs(float(s[2]) * 1e-5 - 127.0) < 127.0 * 1e-6
+    # tiny but non-zero token below the floor: still divided by the floor
+    xt = np.full((1, 128), 1e-7, dtype=np.float32)
+    qt, st, _ = orc.quant_act(xt)
+    assert st[0] == s[2] and (qt == 1).all()   # 1e-7 * 1.27e7 = 1.27 -> 1
+
+
+def test_quant_scale_is_exact_division(orc):
+    # s is the correctly rounded fp32 value of 127 / max|x| (IEEE division):
+    # exactly representable cases pin it without retyping the formula.
+    for amax, s_exact in ((127.0, 1.0), (254.0, 0.5), (2.0, 63.5), (0.5, 254.0)):
+        x = np.zeros((1, 128), dtype=np.float32)
+        x[0, 5] = amax
+        _, s, _ = orc.quant_act(x)
+        assert float(s[0]) == s_exact
+
+
+def test_quant_round_half_even(orc):
+    # amax 127 -> s = 1 exactly, so q = round(x) on exact halves.
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, 0] = 127.0
+    halves = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 126.5]
+    expect = [0, 2, 2, 4, 0, -2, -2, 126]
+    x[0, 1:1 + len(halves)] = halves
+    q, _, _ = orc.quant_act(x)
+    assert q[0, 1:1 + len(halves)].tolist() == expect
+    # amax 2 -> s = 63.5: x = 1 gives 63.5 -> 64, x = -1 -> -64, x = 0.5 -> 31.75 -> 32
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, :4] = [2.0, 1.0, -1.0, 0.5]
+    q, _, _ = orc.quant_act(x)
+    assert q[0, :4].tolist() == [127, 64, -64, 32]
+
+
+def test_quant_rounding_error_bound(orc):
+    # |x - q/s| <= 0.5/s elementwise (rounding to nearest), q within [-127,127].
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((8, 2560), dtype=np.float32) * np.float32(3.0)
+    q, s, _ = orc.quant_act(x)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) / s[:, None].astype(np.float64))
+    assert (err <= 0.5 / s[:, None].astype(np.float64) * (1 + 1e-6)).all()
+    assert np.abs(q.astype(np.int32)).max() <= 127
+
+
+def test_quant_outlier_row(orc):
+    rng = synth.rng_for("b2_sparse", 0, "q", "act")
+    xb = synth.tokens_bf16(rng, 4, 2560, outliers=True,
+                           orng=synth.rng_for("b2_sparse", 0, "q", "outlier"))
+    x = synth.bf16_bits_to_f32(xb)
+    q, s, _ = orc.quant_act(xb)
+    for n in (1, 3):
+        k = int(np.argmax(np.abs(x[n])))
+        assert abs(float(x[n, k])) == 20.0
+        assert abs(int(q[n, k])) == 127
+        rest = np.delete(np.abs(q[n].astype(np.int32)), k)
+        bound = int(np.ceil(127 * np.delete(np.abs(x[n]), k).max() / 20.0))
+        assert rest.max() <= bound <= 30
+
+
+def test_quant_bf16_equals_exact_f32(orc):
+    rng = np.random.default_rng(3)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((5, 640), dtype=np.float32))
+    xf = synth.bf16_bits_to_f32(xb)
+    np.testing.assert_array_equal(orc.bf16_to_f32(xb[0, :16]), xf[0, :16])
+    a = orc.quant_act(xb)
+    b = orc.quant_act(np.ascontiguousarray(xf))
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+# ------------------------------------------------------- epilogue
+def test_epilogue_closed_forms(orc):
+    D = np.array([[0, 1, -1, 1000, -3641344]], dtype=np.int64)
+    s = np.array([2.0], dtype=np.float32)
+    y = orc.epilogue(D, 0.25, s)
+    assert y[0, 0] == 0.0
+    # alpha/s = 1/8 exactly, so every value is exact in binary64
+    assert y[0, 1:].tolist() == [0.125, -0.125, 125.0, -455168.0]
+
+
+def test_epilogue_dequantises_the_float_product(orc):
+    # y approximates alpha * W @ x: the only error is the activation rounding,
+    # |y - alpha * sum_k w x| <= alpha * sum_k |w| * 0.5 / s.  Swapping the
+    # roles of alpha and s, or multiplying by s, breaks this bound.
+    rng = np.random.default_rng(23)
+    M, K, N = 40, 1024, 3
+    W = synth.ternary(rng, M, K)
+    alpha = 0.0625
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    q, s, _ = orc.quant_act(x)
+    y = orc.epilogue(orc.dot_def(W, q), alpha, s)
+    exact = alpha * (x.astype(np.float64) @ W.astype(np.float64).T)
+    bound = alpha * np.abs(W).sum(1)[None, :] * 0.5 / s[:, None].astype(np.float64)
+    assert (np.abs(y - exact) <= bound * (1 + 1e-9)).all()
+    assert np.abs(y - exact).max() > 0  # the bound is not vacuous
+
+
+# ------------------------------------------------------- threaded driver
+def test_linear_driver_matches_pieces(orc):
+    rng = np.random.default_rng(31)
+    M, K, N = 57, 640, 4
+    W = synth.ternary(rng, M, K)
+    P, _ = orc.pack_i2s(W)
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    q, s, qs = orc.quant_act(x)
+    D = orc.dot_def(W, q)
+    y = orc.epilogue(D, 0.03, s)
+    for nt in (1, 3, 8):
+        D2, y2 = orc.linear_i2s(P, K, q, s, np.float32(0.03), nthreads=nt)
+        np.testing.assert_array_equal(D2, D)
+        np.testing.assert_allclose(y2, orc.epilogue(D, float(np.float32(0.03)), s), rtol=1e-15)
+    D3, _ = orc.linear_i2s(P, K, q, s, np.float32(0.03), rows=(10, 20), nthreads=2)
+    np.testing.assert_array_equal(D3, D[:, 10:30])
+    assert y.shape == (N, M)
+
+
+# ------------------------------------------------------- stored regression
+def test_stored_regression_values(orc):
+    """Values written by tests/golden/make_golden.py (oracle only)."""
+    path = os.path.join(GOLDEN, "oracle_single_rows.txt")
+    _, kv = _fixture("oracle_single_rows.txt")
+    W, alpha = synth.matrix("single", "w")
+    x = synth.activations("single", "w", 1)
+    q, s, qs = orc.quant_act(x)
+    assert int(qs[0]) == kv["qsum"][0]
+    P, _ = orc.pack_i2s(W)
+    assert [int(b) for b in P[0, :16]] == kv["packed_row0_first16"]
+    R, D = orc.dot_raw(P, q, qs, W.shape[1])
+    rows = kv["rows"]
+    assert [int(D[0, r]) for r in rows] == kv["dot"]
+    assert os.path.exists(path)
