@@ -1,0 +1,10 @@
+"""MI355X-native BitNet b1.58 W2A8 (I2_S) matmul: Python binding.
+
+The compute lives in ``libbitnet_i2s.so`` (hand-written HIP for gfx950,
+C ABI declared in ``include/bitnet_i2s.h``).  This package only marshals
+torch tensors into that ABI; it loads the library lazily and raises if it
+is missing -- there is no fallback path.
+"""
+from ._binding import (  # noqa: F401
+    BitnetError, abi_version, gemm, gemv, lib_path, load, pack, quant_act,
+)

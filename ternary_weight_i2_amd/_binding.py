@@ -1,0 +1,141 @@
+"""ctypes binding of libbitnet_i2s.so (C ABI in include/bitnet_i2s.h).
+
+Argument marshalling only: each function checks dtype/device/contiguity of
+its torch tensors, passes ``data_ptr()`` and the current HIP stream, and
+raises ``BitnetError`` on a non-zero status.  Every step of the computation
+runs in the library's HIP kernels; nothing here computes a result.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbitnet_i2s.so")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_VALUE, E_HIP = range(7)
+F32, BF16 = 0, 1
+GEMV_MAX_N = 64
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"bitnet status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
+    L.bitnet_pack_i2s.argtypes = [p, i64, i64, p, p]
+    L.bitnet_quant_act_i8.argtypes = [p, ctypes.c_int, i64, i64, p, p, p, p]
+    sig = [p, f32, i64, i64, p, p, p, i64, p, p, p]
+    L.bitnet_gemv_i2s_i8.argtypes = sig
+    L.bitnet_gemm_i2s_i8.argtypes = sig
+    for fn in ("bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
+               "bitnet_gemm_i2s_i8", "bitnet_abi_version"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.bitnet_abi_version.argtypes = []
+    L.bitnet_last_error.argtypes = []
+    L.bitnet_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = load().bitnet_last_error().decode(errors="replace")
+        raise BitnetError(status, msg)
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def abi_version() -> int:
+    return load().bitnet_abi_version()
+
+
+def pack(w):
+    """int8 ternary W[M][K] (cuda) -> uint8 I2_S packed[M][K/4]."""
+    import torch
+    if w.dtype != torch.int8 or w.dim() != 2:
+        raise TypeError("w must be a 2-D int8 tensor")
+    M, K = w.shape
+    out = torch.empty((M, K // 4 if K % 4 == 0 else 0), dtype=torch.uint8, device=w.device)
+    _check(load().bitnet_pack_i2s(_ptr(w), M, K, _ptr(out), _stream(w)))
+    return out
+
+
+def quant_act(x, out=None):
+    """fp32 or bf16 x[N][K] (cuda) -> (int8 xq[N][K], fp32 s[N], int32 xsum[N])."""
+    import torch
+    if x.dim() != 2:
+        raise TypeError("x must be 2-D [N][K]")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError("x must be float32 or bfloat16")
+    N, K = x.shape
+    if out is None:
+        xq = torch.empty((N, K), dtype=torch.int8, device=x.device)
+        s = torch.empty((N,), dtype=torch.float32, device=x.device)
+        xs = torch.empty((N,), dtype=torch.int32, device=x.device)
+    else:
+        xq, s, xs = out
+    _check(load().bitnet_quant_act_i8(_ptr(x), dt, N, K, _ptr(xq), _ptr(s),
+                                      _ptr(xs), _stream(x)))
+    return xq, s, xs
+
+
+def _matmul(fn, packed, w_scale, K, xq, x_scale, x_sum, want_dot, want_y, out):
+    import torch
+    M = packed.shape[0]
+    N = xq.shape[0]
+    if out is not None:
+        dot, y = out
+    else:
+        dot = torch.empty((N, M), dtype=torch.int32, device=xq.device) if want_dot else None
+        y = torch.empty((N, M), dtype=torch.float32, device=xq.device) if want_y else None
+    _check(fn(_ptr(packed), float(w_scale), M, K, _ptr(xq), _ptr(x_scale),
+              _ptr(x_sum), N, _ptr(dot), _ptr(y), _stream(xq)))
+    return dot, y
+
+
+def gemv(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
+    """Decode matmul (1..64 tokens) -> (int32 dot[N][M] | None, fp32 y[N][M] | None)."""
+    K = xq.shape[1]
+    return _matmul(load().bitnet_gemv_i2s_i8, packed, w_scale, K, xq, x_scale,
+                   x_sum, want_dot, want_y, out)
+
+
+def gemm(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
+    """Prefill matmul (any token count, int8 MFMA) -> (dot | None, y | None)."""
+    K = xq.shape[1]
+    return _matmul(load().bitnet_gemm_i2s_i8, packed, w_scale, K, xq, x_scale,
+                   x_sum, want_dot, want_y, out)

@@ -1,0 +1,175 @@
+// abi.hip -- the C ABI of libbitnet_i2s.so (declared in include/bitnet_i2s.h):
+// host-side argument validation, error reporting and kernel dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+
+#include "bitnet_i2s.h"
+#include "common.h"
+
+#define BITNET_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return BITNET_OK;
+}
+
+int hip_fail(const char *where, hipError_t e) {
+    return fail(BITNET_E_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_k(const char *fn, int64_t K) {
+    if (K <= 0 || K % bitnet::kBlock != 0 || K > BITNET_MAX_K)
+        return fail(BITNET_E_SHAPE, "%s: K=%lld must be a positive multiple of 128 and <= %d",
+                    fn, (long long)K, BITNET_MAX_K);
+    return BITNET_OK;
+}
+
+// Device-side count of non-ternary weights seen by the packer.  Each device
+// holds its own copy; its address is looked up once per device with
+// hipGetSymbolAddress and only that address is used from the host.
+__device__ unsigned g_pack_bad;
+constexpr int kMaxDevices = 64;
+void *g_pack_bad_addr[kMaxDevices];
+std::mutex g_pack_mu;
+
+int pack_counter(int dev, unsigned **out) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BITNET_E_HIP, "bitnet_pack_i2s: device index %d unsupported", dev);
+    if (!g_pack_bad_addr[dev]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_pack_bad));
+        if (e != hipSuccess) return hip_fail("bitnet_pack_i2s: hipGetSymbolAddress", e);
+        g_pack_bad_addr[dev] = p;
+    }
+    *out = static_cast<unsigned *>(g_pack_bad_addr[dev]);
+    return BITNET_OK;
+}
+
+int check_matmul(const char *fn, const uint8_t *packed, int64_t M, int64_t K,
+                 const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                 int64_t max_n, const int32_t *dot, const float *y) {
+    if (M < 0 || N < 0)
+        return fail(BITNET_E_SHAPE, "%s: negative size M=%lld N=%lld", fn, (long long)M,
+                    (long long)N);
+    if (M > 0x7fffffffLL)
+        return fail(BITNET_E_SHAPE, "%s: M=%lld exceeds 2^31-1", fn, (long long)M);
+    if (N > max_n)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld exceeds %lld", fn, (long long)N,
+                    (long long)max_n);
+    if (int s = check_k(fn, K)) return s;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!packed || !xq || !xs || !xsum)
+        return fail(BITNET_E_NULL, "%s: packed, xq, x_scale and x_sum are required", fn);
+    if (!dot && !y) return fail(BITNET_E_NULL, "%s: dot and y are both NULL", fn);
+    if (!aligned(packed, 16) || !aligned(xq, 16))
+        return fail(BITNET_E_ALIGN, "%s: packed and xq must be 16-byte aligned", fn);
+    if (!aligned(xs, 4) || !aligned(xsum, 4) || (dot && !aligned(dot, 4)) ||
+        (y && !aligned(y, 4)))
+        return fail(BITNET_E_ALIGN, "%s: x_scale, x_sum, dot, y must be 4-byte aligned", fn);
+    return BITNET_OK;
+}
+
+}  // namespace
+
+BITNET_API int bitnet_abi_version(void) { return BITNET_ABI_VERSION; }
+
+BITNET_API const char *bitnet_last_error(void) { return g_last_error.c_str(); }
+
+BITNET_API int bitnet_pack_i2s(const int8_t *w, int64_t M, int64_t K, uint8_t *packed,
+                               void *stream) {
+    const char *fn = "bitnet_pack_i2s";
+    if (M < 0) return fail(BITNET_E_SHAPE, "%s: negative M=%lld", fn, (long long)M);
+    if (int s = check_k(fn, K)) return s;
+    if (M == 0) return ok();
+    if (!w || !packed) return fail(BITNET_E_NULL, "%s: w and packed are required", fn);
+    if (!aligned(w, 4) || !aligned(packed, 16))
+        return fail(BITNET_E_ALIGN, "%s: w must be 4-byte and packed 16-byte aligned", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("bitnet_pack_i2s: hipGetDevice", e);
+    unsigned *bad = nullptr;
+    if (int s = pack_counter(dev, &bad)) return s;
+    if ((e = hipMemsetAsync(bad, 0, sizeof(unsigned), st)) != hipSuccess)
+        return hip_fail("bitnet_pack_i2s: clear counter", e);
+    if ((e = bitnet::launch_pack(w, M, K, packed, bad, st)) != hipSuccess)
+        return hip_fail("bitnet_pack_i2s: launch", e);
+    unsigned nbad = 0;
+    if ((e = hipMemcpyAsync(&nbad, bad, sizeof nbad, hipMemcpyDeviceToHost, st)) != hipSuccess)
+        return hip_fail("bitnet_pack_i2s: read counter", e);
+    if ((e = hipStreamSynchronize(st)) != hipSuccess)
+        return hip_fail("bitnet_pack_i2s: synchronize", e);
+    if (nbad)
+        return fail(BITNET_E_VALUE, "%s: %u weight(s) outside {-1,0,+1}", fn, nbad);
+    return ok();
+}
+
+BITNET_API int bitnet_quant_act_i8(const void *x, int dtype, int64_t N, int64_t K, int8_t *xq,
+                                   float *x_scale, int32_t *x_sum, void *stream) {
+    const char *fn = "bitnet_quant_act_i8";
+    if (dtype != BITNET_F32 && dtype != BITNET_BF16)
+        return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (N < 0 || N > 0x7fffffffLL)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    if (int s = check_k(fn, K)) return s;
+    if (N == 0) return ok();
+    if (!x || !xq || !x_scale || !x_sum)
+        return fail(BITNET_E_NULL, "%s: x, xq, x_scale and x_sum are required", fn);
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+        return fail(BITNET_E_ALIGN, "%s: x and xq must be 16-byte aligned", fn);
+    hipError_t e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("bitnet_quant_act_i8: launch", e);
+    return ok();
+}
+
+BITNET_API int bitnet_gemv_i2s_i8(const uint8_t *packed, float w_scale, int64_t M, int64_t K,
+                                  const int8_t *xq, const float *x_scale,
+                                  const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
+                                  void *stream) {
+    const char *fn = "bitnet_gemv_i2s_i8";
+    if (int s = check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, BITNET_GEMV_MAX_N, dot, y))
+        return s;
+    if (M == 0 || N == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = N <= 8 ? bitnet::launch_gemv_valu(packed, w_scale, M, K, xq, x_scale, x_sum,
+                                                     N, dot, y, st)
+                          : bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum,
+                                                     N, dot, y, st);
+    if (e != hipSuccess) return hip_fail("bitnet_gemv_i2s_i8: launch", e);
+    return ok();
+}
+
+BITNET_API int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t M, int64_t K,
+                                  const int8_t *xq, const float *x_scale,
+                                  const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
+                                  void *stream) {
+    const char *fn = "bitnet_gemm_i2s_i8";
+    if (int s = check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, BITNET_GEMM_MAX_N, dot, y))
+        return s;
+    if (M == 0 || N == 0) return ok();
+    hipError_t e = bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot,
+                                            y, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("bitnet_gemm_i2s_i8: launch", e);
+    return ok();
+}

@@ -1,0 +1,162 @@
+// pack_quant.hip -- I2_S packing and per-token absmax int8 quantisation.
+//
+// Pages: [P1] "BitNet 딥다이브" (fiv.co.kr), §1-1 code table, §4-2 block
+// interleave, §4-5 per-token activation quantisation; [P4] "bitnet.rs",
+// "Mathematical Foundation" (8-bit activation clip range).
+#include "common.h"
+
+namespace bitnet {
+
+// ---------------------------------------------------------------------------
+// Packing [P1 §1-1, §4-2].  One thread builds one packed dword = bytes
+// g0..g0+3 of a 32-byte block, i.e. block positions g0+e+32*i for e, i in
+// 0..3.  For each group i the four source weights are contiguous in the row,
+// so the thread issues four aligned 32-bit loads and one 32-bit store.
+// A weight outside {-1,0,+1} is counted in *bad and stored as code 3.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_i2s_kernel(
+    const int8_t *__restrict__ w, int64_t M, int64_t K,
+    uint8_t *__restrict__ packed, unsigned *__restrict__ bad) {
+    const int64_t dw_per_row = K / 16;
+    const int64_t total = M * dw_per_row;
+    unsigned nbad = 0;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+         d += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = d / dw_per_row;
+        const int64_t r = d - m * dw_per_row;
+        const int64_t blk = r >> 3;          // 8 dwords per block
+        const int g0 = (int)(r & 7) * 4;     // first block byte of this dword
+        const int8_t *src = w + m * K + blk * kBlock + g0;
+        uint32_t out = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(src + 32 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int code = (int)(int8_t)(v >> (8 * e)) + 1;   // -1,0,+1 -> 0,1,2
+                if ((unsigned)code > 2u) {
+                    ++nbad;
+                    code = 3;
+                }
+                out |= (uint32_t)code << (8 * e + 6 - 2 * i);
+            }
+        }
+        *reinterpret_cast<uint32_t *>(packed + m * (K / 4) + blk * kBlockBytes + g0) = out;
+    }
+    if (nbad) atomicAdd(bad, nbad);
+}
+
+hipError_t launch_pack(const int8_t *w, int64_t M, int64_t K, uint8_t *packed,
+                       unsigned *bad, hipStream_t st) {
+    const int64_t total = M * (K / 16);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_i2s_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       w, M, K, packed, bad);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-token quantisation [P1 §4-5]: s = 127 / max(max|x|, 1e-5),
+// q = clamp(round_half_even(x*s), -128, 127) [P4], plus sum(q).
+// One 256-thread workgroup per token; 16-byte loads (4 fp32 or 8 bf16).
+// s is the correctly rounded fp32 quotient: the division is done in binary64
+// and rounded once to binary32, which equals the correctly rounded binary32
+// quotient of the two fp32 operands (53 >= 2*24 + 2).
+// ---------------------------------------------------------------------------
+template <int BF16>
+struct Vec16;   // 16 bytes of activations widened to fp32
+
+template <>
+struct Vec16<0> {
+    static constexpr int kElems = 4;
+    __device__ static void load(const void *base, int64_t i, float *v) {
+        const float4 f = reinterpret_cast<const float4 *>(base)[i];
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+};
+
+template <>
+struct Vec16<1> {
+    static constexpr int kElems = 8;
+    __device__ static void load(const void *base, int64_t i, float *v) {
+        const uint4 u = reinterpret_cast<const uint4 *>(base)[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(w[j] << 16);            // low half = lower element
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+};
+
+template <int BF16>
+__global__ __launch_bounds__(256) void quant_act_kernel(
+    const void *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
+    float *__restrict__ xs, int32_t *__restrict__ xsum) {
+    using V = Vec16<BF16>;
+    constexpr int E = V::kElems;
+    __shared__ float red_f[4];
+    __shared__ int red_i[4];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const char *row = reinterpret_cast<const char *>(x) + n * K * (BF16 ? 2 : 4);
+    const int64_t nvec = K / E;
+
+    float a = 0.0f;
+    for (int64_t i = tid; i < nvec; i += 256) {
+        float v[E];
+        V::load(row, i, v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(v[e]));
+    }
+    a = wave_max_f32(a);
+    if (lane == 0) red_f[wv] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    const float denom = a > 1e-5f ? a : 1e-5f;
+    const float s = (float)(127.0 / (double)denom);
+
+    int8_t *qrow = xq + n * K;
+    int sum = 0;
+    for (int64_t i = tid; i < nvec; i += 256) {
+        float v[E];
+        V::load(row, i, v);
+        uint32_t packedq[E / 4];
+#pragma unroll
+        for (int j = 0; j < E / 4; ++j) packedq[j] = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float r = __builtin_rintf(v[e] * s);
+            r = fminf(fmaxf(r, -128.0f), 127.0f);
+            const int qi = (int)r;
+            sum += qi;
+            packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+        }
+        if (E == 8) {
+            reinterpret_cast<uint2 *>(qrow)[i] = make_uint2(packedq[0], packedq[E / 4 - 1]);
+        } else {
+            reinterpret_cast<uint32_t *>(qrow)[i] = packedq[0];
+        }
+    }
+    sum = wave_sum_i32(sum);
+    if (lane == 0) red_i[wv] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        xs[n] = s;
+        xsum[n] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+    }
+}
+
+hipError_t launch_quant(const void *x, int bf16, int64_t N, int64_t K,
+                        int8_t *xq, float *xs, int32_t *xsum, hipStream_t st) {
+    if (bf16)
+        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)N), dim3(256), 0, st,
+                           x, K, xq, xs, xsum);
+    else
+        hipLaunchKernelGGL(quant_act_kernel<0>, dim3((unsigned)N), dim3(256), 0, st,
+                           x, K, xq, xs, xsum);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -131,3 +131,36 @@ def activations(workload: str, proj: str, N: int, layer: int = 0) -> np.ndarray:
         return tokens_f32(r, N, K)
     return tokens_bf16(r, N, K, outliers=(workload == "b2_sparse"),
                        orng=rng_for(workload, layer, proj, "outlier"))
+
+
+# ---- device-side draws for large benchmark stacks ---------------------------
+# Hundreds of MB of weights are drawn directly on the GPU with torch's seeded
+# generator (no arithmetic of the method involved); tests draw on the host.
+
+def ternary_torch(M: int, K: int, seed: int, device="cuda", dist: str = "uniform"):
+    """int8 [M][K] ternary tensor drawn on ``device`` with a seeded generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if dist == "uniform":
+        return torch.randint(0, 3, (M, K), dtype=torch.int8, device=device, generator=g) - 1
+    if dist == "half_zero":
+        u = torch.randint(0, 4, (M, K), dtype=torch.int8, device=device, generator=g)
+        out = torch.zeros((M, K), dtype=torch.int8, device=device)
+        out[u == 2] = 1
+        out[u == 3] = -1
+        return out
+    raise ValueError(dist)
+
+
+def tokens_bf16_torch(N: int, K: int, seed: int, device="cuda"):
+    """bf16 [N][K] ~ N(0,1) drawn on ``device`` (fp32 sample rounded to bf16)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randn((N, K), dtype=torch.float32, device=device, generator=g).to(torch.bfloat16)
+
+
+def stack_seed(workload: str, layer: int, proj: str, role: str) -> int:
+    """A 63-bit seed for device-side draws, derived like ``rng_for``."""
+    return int(rng_for(workload, layer, proj, role).integers(0, 2 ** 63 - 1))

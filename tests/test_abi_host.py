@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (CPU only: nothing is launched).
+
+The library must load, export every function include/bitnet_i2s.h declares,
+and reject bad arguments with the documented status before touching the
+device.  Fake pointer values are never dereferenced: every case below fails
+validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet_i2s.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_VALUE, E_HIP = range(7)
+FAKE = 0x10000          # 64 KiB-aligned non-null value, never dereferenced
+MIS = 0x10004           # 4- but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    from ternary_weight_i2_amd import _binding
+    return _binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(bitnet_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    fns = set(declared_functions())
+    assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
+            "bitnet_gemm_i2s_i8", "bitnet_last_error", "bitnet_abi_version"} <= fns
+
+
+def test_library_exports_every_declared_symbol(L):
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_abi_version(L):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define BITNET_ABI_VERSION (\d+)", text).group(1))
+    assert L.bitnet_abi_version() == v
+
+
+def _err(L):
+    return L.bitnet_last_error().decode()
+
+
+def test_pack_validation(L):
+    assert L.bitnet_pack_i2s(FAKE, 4, 100, FAKE, None) == E_SHAPE
+    assert "multiple of 128" in _err(L)
+    assert L.bitnet_pack_i2s(FAKE, -1, 128, FAKE, None) == E_SHAPE
+    assert L.bitnet_pack_i2s(FAKE, 4, 0, FAKE, None) == E_SHAPE
+    assert L.bitnet_pack_i2s(FAKE, 4, 65536 + 128, FAKE, None) == E_SHAPE
+    assert L.bitnet_pack_i2s(None, 4, 128, FAKE, None) == E_NULL
+    assert L.bitnet_pack_i2s(FAKE, 4, 128, None, None) == E_NULL
+    assert L.bitnet_pack_i2s(FAKE + 1, 4, 128, FAKE, None) == E_ALIGN
+    assert L.bitnet_pack_i2s(FAKE, 4, 128, MIS, None) == E_ALIGN
+    # M == 0 is a no-op, even with NULL pointers
+    assert L.bitnet_pack_i2s(None, 0, 128, None, None) == OK
+
+
+def test_quant_validation(L):
+    q = L.bitnet_quant_act_i8
+    assert q(FAKE, 2, 1, 128, FAKE, FAKE, FAKE, None) == E_DTYPE
+    assert q(FAKE, 0, 1, 96, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert q(FAKE, 0, -2, 128, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert q(None, 0, 1, 128, FAKE, FAKE, FAKE, None) == E_NULL
+    assert q(FAKE, 1, 1, 128, FAKE, None, FAKE, None) == E_NULL
+    assert q(MIS, 1, 1, 128, FAKE, FAKE, FAKE, None) == E_ALIGN
+    assert q(FAKE, 1, 1, 128, MIS, FAKE, FAKE, None) == E_ALIGN
+    assert q(FAKE, 1, 1, 128, FAKE, FAKE + 2, FAKE, None) == E_ALIGN
+    assert q(None, 1, 0, 128, None, None, None, None) == OK
+
+
+@pytest.mark.parametrize("name,maxn", [("bitnet_gemv_i2s_i8", 64),
+                                       ("bitnet_gemm_i2s_i8", 1 << 21)])
+def test_matmul_validation(L, name, maxn):
+    f = getattr(L, name)
+    a = dict(packed=FAKE, s=0.05, M=16, K=256, xq=FAKE, xs=FAKE, xsum=FAKE, N=1,
+             dot=FAKE, y=FAKE)
+
+    def call(**kw):
+        b = dict(a, **kw)
+        return f(b["packed"], b["s"], b["M"], b["K"], b["xq"], b["xs"], b["xsum"],
+                 b["N"], b["dot"], b["y"], None)
+
+    assert call(K=200) == E_SHAPE
+    assert call(K=0) == E_SHAPE
+    assert call(M=-1) == E_SHAPE
+    assert call(N=-1) == E_SHAPE
+    assert call(N=maxn + 1) == E_SHAPE
+    assert call(M=1 << 31) == E_SHAPE
+    assert call(packed=None) == E_NULL
+    assert call(xq=None) == E_NULL
+    assert call(xs=None) == E_NULL
+    assert call(xsum=None) == E_NULL
+    assert call(dot=None, y=None) == E_NULL
+    assert call(packed=MIS) == E_ALIGN
+    assert call(xq=MIS) == E_ALIGN
+    assert call(y=FAKE + 2) == E_ALIGN
+    assert call(dot=FAKE + 1) == E_ALIGN
+    assert call(M=0, packed=None, xq=None) == OK
+    assert call(N=0, packed=None, xq=None) == OK
+    assert _err(L) == ""
+
+
+def test_last_error_is_per_thread(L):
+    import threading
+    assert L.bitnet_pack_i2s(FAKE, 4, 100, FAKE, None) == E_SHAPE
+    seen = {}
+
+    def other():
+        seen["msg"] = L.bitnet_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "multiple of 128" in _err(L)
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from ternary_weight_i2_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _binding.load()
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # the package and the C sources must not import, link or name the oracle
+    pkg = os.path.join(ROOT, "ternary_weight_i2_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "bitnet_oracle" not in text and "liboracle" not in text, fn

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Integers (packed bytes, int8 activations, int32 sums and dots) must match
+bit for bit.  fp32 outputs must satisfy |y - y_ref| <= 1e-5 |y_ref| against
+the oracle's float64 y_ref, and be exactly 0 where the dot is 0.  The
+quantisation scale s is compared bit for bit (both sides form the correctly
+rounded fp32 quotient and take every rounding decision in fp32).
+
+Inputs come from the seeded generators only; the oracle receives the host
+copies of those inputs and computes its own packing and quantisation.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_i2_amd import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+Y_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def bn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ternary_weight_i2_amd as bn
+    bn.load()
+    oracle.lib()
+    return bn
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_bf16_tensor(bits):
+    return dev(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def check_y(y, D, alpha, s):
+    y_ref = oracle.epilogue(D, alpha, s)
+    y = y.astype(np.float64)
+    err = np.abs(y - y_ref)
+    assert (err <= Y_RTOL * np.abs(y_ref)).all(), float((err / np.maximum(np.abs(y_ref), 1e-30)).max())
+    assert (y[D == 0] == 0).all()
+
+
+def gpu_linear(bn, P_gpu, alpha, xq, xs, xsum, entry):
+    fn = bn.gemv if entry == "gemv" else bn.gemm
+    dot, y = fn(P_gpu, alpha, xq, xs, xsum)
+    torch.cuda.synchronize()
+    return dot.cpu().numpy(), y.cpu().numpy()
+
+
+def run_case(bn, M, K, N, entry, dist="uniform", seed=0, act="bf16", outliers=False,
+             rows=None):
+    """Full pipeline on GPU vs oracle; ``rows`` = list of (start, count) to sample."""
+    rng = np.random.default_rng(seed)
+    W = synth.ternary(rng, M, K, dist)
+    alpha = synth.weight_scale(rng)
+    if act == "f32":
+        x = synth.tokens_f32(rng, N, K)
+        x_gpu = dev(x)
+    else:
+        x = synth.tokens_bf16(rng, N, K, outliers=outliers)
+        x_gpu = to_bf16_tensor(x)
+    # GPU path
+    P_gpu = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(x_gpu)
+    dot, y = gpu_linear(bn, P_gpu, alpha, xq, xs, xsum, entry)
+    # oracle path
+    q, s, qs = oracle.quant_act(x)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs)
+    spans = rows if rows is not None else [(0, M)]
+    P_host = P_gpu.cpu().numpy()
+    for r0, nr in spans:
+        Pr, bad = oracle.pack_i2s(W[r0:r0 + nr])
+        assert bad == 0
+        np.testing.assert_array_equal(P_host[r0:r0 + nr], Pr)
+        D, _ = oracle.linear_i2s(Pr, K, q, s, alpha, nthreads=8, want_y=False)
+        assert np.abs(D).max() < 2 ** 31
+        np.testing.assert_array_equal(dot[:, r0:r0 + nr], D)
+        check_y(y[:, r0:r0 + nr], D, alpha, s)
+    return dot, y
+
+
+# ------------------------------------------------------------------ pack
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (257, 640), (2560, 2560), (640, 6912)])
+def test_pack_bit_exact(bn, M, K):
+    rng = np.random.default_rng(M + K)
+    for dist in ("uniform", "half_zero"):
+        W = synth.ternary(rng, M, K, dist)
+        P = bn.pack(dev(W)).cpu().numpy()
+        Pr, _ = oracle.pack_i2s(W)
+        np.testing.assert_array_equal(P, Pr)
+
+
+def test_pack_rejects_non_ternary(bn):
+    W = np.zeros((5, 256), dtype=np.int8)
+    W[3, 17] = 2
+    W[0, 255] = -128
+    with pytest.raises(bn.BitnetError) as ei:
+        bn.pack(dev(W))
+    assert ei.value.status == 5
+    assert "2 weight" in str(ei.value)
+    # the next call on the same device starts from a clean count
+    W[3, 17] = 1
+    W[0, 255] = -1
+    P = bn.pack(dev(W)).cpu().numpy()
+    np.testing.assert_array_equal(P, oracle.pack_i2s(W)[0])
+
+
+# ------------------------------------------------------------------ quant
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 512), (17, 2560), (5, 6912), (2, 65536)])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_quant_bit_exact(bn, N, K, act):
+    rng = np.random.default_rng(N * 7 + K)
+    if act == "f32":
+        x = synth.tokens_f32(rng, N, K) * np.float32(rng.uniform(0.01, 50))
+        xg = dev(x)
+    else:
+        x = synth.tokens_bf16(rng, N, K, outliers=True)
+        xg = to_bf16_tensor(x)
+    xq, xs, xsum = bn.quant_act(xg)
+    q, s, qs = oracle.quant_act(x)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs)
+
+
+def test_quant_edge_rows(bn):
+    K = 256
+    x = np.zeros((6, K), dtype=np.float32)
+    x[1, :] = 0.37                      # constant row -> all 127
+    x[2, 0] = 127.0                     # s = 1: exact halves round to even
+    x[2, 1:9] = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 126.5]
+    x[3, :] = 1e-7                      # below the 1e-5 floor
+    x[4, 0] = 2.0                       # s = 63.5 -> ties at 63.5
+    x[4, 1:4] = [1.0, -1.0, 0.5]
+    x[5, 7] = -3.0e38                   # huge magnitude
+    x[5, 8] = 1.0e-38
+    xq, xs, xsum = bn.quant_act(dev(x))
+    q, s, qs = oracle.quant_act(x)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs)
+    assert q[2, 1:9].tolist() == [0, 2, 2, 4, 0, -2, -2, 126]
+
+
+# ------------------------------------------------------ small-shape matmuls
+SMALL = [(1, 128, 1), (5, 128, 2), (17, 384, 3), (64, 256, 4), (100, 640, 5),
+         (129, 1152, 8), (33, 512, 9), (70, 896, 16), (130, 256, 31), (65, 384, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL)
+def test_gemv_small(bn, M, K, N):
+    run_case(bn, M, K, N, "gemv", seed=M * 131 + K + N)
+
+
+@pytest.mark.parametrize("M,K,N", SMALL + [(200, 1024, 128), (77, 640, 300), (300, 256, 129)])
+def test_gemm_small(bn, M, K, N):
+    run_case(bn, M, K, N, "gemm", seed=M * 17 + K * 3 + N)
+
+
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_optional_outputs_and_zero_sizes(bn, entry):
+    rng = np.random.default_rng(1)
+    M, K, N = 48, 256, 3
+    W = synth.ternary(rng, M, K)
+    P = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(dev(synth.tokens_f32(rng, N, K)))
+    fn = bn.gemv if entry == "gemv" else bn.gemm
+    d_only, none_y = fn(P, 0.5, xq, xs, xsum, want_y=False)
+    none_d, y_only = fn(P, 0.5, xq, xs, xsum, want_dot=False)
+    d_both, y_both = fn(P, 0.5, xq, xs, xsum)
+    torch.cuda.synchronize()
+    assert none_y is None and none_d is None
+    assert torch.equal(d_only, d_both) and torch.equal(y_only, y_both)
+    # N == 0 and M == 0 are no-ops
+    e = torch.empty((0, K), dtype=torch.int8, device="cuda")
+    fn(P, 0.5, e, xs[:0], xsum[:0])
+    fn(P[:0], 0.5, xq, xs, xsum)
+
+
+def test_special_weights(bn):
+    # all -1, all 0, all +1 rows: D = -sum(q), 0, +sum(q)
+    K, N = 512, 4
+    W = np.zeros((3 * 40, K), dtype=np.int8)
+    W[:40] = -1
+    W[80:] = 1
+    rng = np.random.default_rng(2)
+    x = synth.tokens_bf16(rng, N, K)
+    P = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(to_bf16_tensor(x))
+    for fn in (bn.gemv, bn.gemm):
+        dot, y = fn(P, 0.07, xq, xs, xsum)
+        d = dot.cpu().numpy()
+        qs = xsum.cpu().numpy()
+        assert (d[:, :40] == -qs[:, None]).all()
+        assert (d[:, 40:80] == 0).all() and (y.cpu().numpy()[:, 40:80] == 0).all()
+        assert (d[:, 80:] == qs[:, None]).all()
+
+
+def test_extreme_activations_max_k(bn):
+    # every activation at +-127 with K = 65536: the largest |D| the ABI allows
+    K, M, N = 65536, 8, 2
+    W = np.ones((M, K), dtype=np.int8)
+    W[1::2] = -1
+    x = np.full((N, K), 3.0, dtype=np.float32)
+    x[1] = -3.0
+    P = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(dev(x))
+    for fn in (bn.gemv, bn.gemm):
+        dot, _ = fn(P, 1.0, xq, xs, xsum)
+        d = dot.cpu().numpy()
+        assert d[0, 0] == 127 * K and d[0, 1] == -127 * K
+        assert d[1, 0] == -127 * K and d[1, 1] == 127 * K
+
+
+def test_deterministic(bn):
+    d1, y1 = run_case(bn, 300, 2560, 4, "gemv", seed=5)
+    d2, y2 = run_case(bn, 300, 2560, 4, "gemv", seed=5)
+    np.testing.assert_array_equal(d1, d2)
+    np.testing.assert_array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# ------------------------------------------------------ workload shapes
+def test_single_matrix_workload(bn):
+    """256x512, uniform ternary, one fp32 token: full comparison."""
+    W, alpha = synth.matrix("single", "w")
+    x = synth.activations("single", "w", 1)
+    P = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(dev(x))
+    dot, y = gpu_linear(bn, P, alpha, xq, xs, xsum, "gemv")
+    q, s, qs = oracle.quant_act(x)
+    Pr, _ = oracle.pack_i2s(W)
+    R, D = oracle.dot_raw(Pr, q, qs, 512)
+    np.testing.assert_array_equal(P.cpu().numpy(), Pr)
+    np.testing.assert_array_equal(dot, D)
+    check_y(y, D, alpha, s)
+
+
+@pytest.mark.parametrize("proj", synth.PROJ_NAMES)
+def test_b2_decode_shapes(bn, proj):
+    M, K = synth.SHAPES["b2"][proj]
+    run_case(bn, M, K, 1, "gemv", seed=synth.PROJ_NAMES.index(proj))
+
+
+@pytest.mark.parametrize("N", [1, 4, 16, 64])
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_b2_batched_decode(bn, proj, N):
+    M, K = synth.SHAPES["b2_sparse"][proj]
+    run_case(bn, M, K, N, "gemv", dist="half_zero", outliers=True, seed=N * 10 + len(proj))
+
+
+@pytest.mark.parametrize("N", [128, 4096])
+@pytest.mark.parametrize("proj", synth.PROJ_NAMES)
+def test_e06_prefill(bn, proj, N):
+    M, K = synth.SHAPES["e06"][proj]
+    rows = None if N == 128 else [(0, 64), (M // 2 - 7, 64), (M - 50, 50)]
+    run_case(bn, M, K, N, "gemm", seed=N + len(proj), rows=rows)
+
+
+@pytest.mark.parametrize("N", [1, 16])
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_large_layer_sampled(bn, proj, N):
+    M, K = synth.SHAPES["large"][proj]
+    rows = [(0, 48), (M // 2 + 5, 48), (M - 33, 33)]
+    run_case(bn, M, K, N, "gemv", seed=N + 100 * len(proj), rows=rows)
