@@ -4,16 +4,17 @@
 Workload: the 2B-class decode stack -- 30 layers x {q, k, v, o, gate, up,
 down} ternary projections (q/o 2560x2560, k/v 640x2560, gate/up 6912x2560,
 down 2560x6912; 521,011,200 packed bytes), one token (N=1) of bf16
-activations per dependency group (q/k/v share one token, gate/up share one,
-o and down each have their own).  One step = for every layer and group:
-per-token int8 quantisation of the bf16 token, then the I2_S GEMV of every
-projection fed by it, writing int32 dots and fp32 outputs.  The packed
-weights (1.7x the 256 MB last-level cache) are re-read from HBM every step.
-The step is captured once in a HIP graph and replayed.
+activations per dependency group: q/k/v share one token, gate/up share one,
+o and down each have their own, as in a decoder layer.  One step = for every
+layer and group, one fused launch that quantises the bf16 token per token
+(absmax int8) and runs the I2_S GEMV of every projection fed by it, writing
+int32 dots and fp32 outputs (4 launches per layer, 120 per step, in
+dependency order).  The packed weights (2x the 256 MB last-level cache) are
+re-read from HBM every step.  The step is captured once in a HIP graph and
+replayed.
 
-Prints ONE JSON line (rank 0).  ``value`` = algorithmic bytes per step /
-step time (GB/s): packed weights + bf16 tokens + per-token scale/sum +
-int32 and fp32 outputs.
+Prints ONE JSON line.  ``value`` = algorithmic bytes per step / step time
+(GB/s): packed weights + bf16 tokens + int32 and fp32 outputs.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
 
@@ -39,6 +41,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the secondary per-row measurements")
     return ap.parse_args()
 
 
@@ -69,34 +73,32 @@ def build_stack(bn, synth, torch, layers):
 
 
 def step_bytes(stack):
+    """Algorithmic bytes of one step: every packed weight byte once, each bf16
+    token once per group, int32 dot + fp32 y per output."""
     b = 0
     for layer in stack:
         for x, xq, xs, xsum, mats in layer["groups"]:
             N, K = x.shape
-            b += N * K * 2 + N * 8                    # bf16 token in, s and sum out
+            b += N * K * 2
             for P, alpha, dot, y, M, K in mats:
-                b += M * K // 4 + N * 8 + N * M * 8   # packed, s+sum in, dot+y out
+                b += M * K // 4 + N * M * 8
     return b
 
 
-def gemv_bytes(stack):
-    b = 0
+def run_step(bn, stack):
+    """The timed step: one fused quantise+GEMV launch per dependency group."""
     for layer in stack:
         for x, xq, xs, xsum, mats in layer["groups"]:
-            N, K = x.shape
+            bn.linear(x, [(m[0], m[1]) for m in mats], out=[(m[2], m[3]) for m in mats])
+
+
+def run_step_unfused(bn, stack):
+    """Same work through the separate calls (quantiser, then one GEMV per matrix)."""
+    for layer in stack:
+        for x, xq, xs, xsum, mats in layer["groups"]:
+            bn.quant_act(x, out=(xq, xs, xsum))
             for P, alpha, dot, y, M, K in mats:
-                b += M * K // 4 + N * K + N * 8 + N * M * 8
-    return b
-
-
-def run_step(bn, stack, quant=True, gemv=True):
-    for layer in stack:
-        for x, xq, xs, xsum, mats in layer["groups"]:
-            if quant:
-                bn.quant_act(x, out=(xq, xs, xsum))
-            if gemv:
-                for P, alpha, dot, y, M, K in mats:
-                    bn.gemv(P, alpha, xq, xs, xsum, out=(dot, y))
+                bn.gemv(P, alpha, xq, xs, xsum, out=(dot, y))
 
 
 def capture(torch, fn):
@@ -163,6 +165,135 @@ def cpu_baseline(seconds):
                       f"unpack + definition dot + epilogue, {el:.1f} s"}
 
 
+def _events_time(torch, fn, reps, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def secondary_rows(bn, synth, torch, stack):
+    """One figure per other hot-path row, each timed with HIP events on the
+    launch stream.  Shapes are the workloads' own; weights reuse the decode
+    stack where the shapes match (so they stream from HBM), else are drawn
+    fresh on the device."""
+    rows = {}
+    # a1: pack (one-time step) -- 6912x2560 int8 -> I2_S
+    M, K = synth.SHAPES["b2"]["gate"]
+    W = synth.ternary_torch(M, K, 11)
+    out = torch.empty((M, K // 4), dtype=torch.uint8, device="cuda")
+    lib = bn.load()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def do_pack():
+        lib.bitnet_pack_i2s(W.data_ptr(), M, K, out.data_ptr(), st)
+    t = _events_time(torch, do_pack, 10)
+    rows["pack"] = {"shape": f"{M}x{K}", "us": round(t * 1e6, 2),
+                    "GB/s": round((M * K + M * K // 4) / t / 1e9, 1),
+                    "note": "includes the stream sync that reads the bad-value count"}
+    del W, out
+    # a2: quantisation of a 4096x1024 bf16 prefill block
+    N, K = 4096, 1024
+    x = synth.tokens_bf16_torch(N, K, 12)
+    o = (torch.empty((N, K), dtype=torch.int8, device="cuda"),
+         torch.empty((N,), dtype=torch.float32, device="cuda"),
+         torch.empty((N,), dtype=torch.int32, device="cuda"))
+    t = _events_time(torch, lambda: bn.quant_act(x, out=o), 50)
+    rows["quant"] = {"shape": f"{N}x{K} bf16", "us": round(t * 1e6, 2),
+                     "GB/s": round((N * K * 3 + N * 8) / t / 1e9, 1)}
+    # a4: batched decode on the 2B stack shapes, N = 4, 16, 64 (weights from HBM)
+    for N in (4, 16, 64):
+        bufs = []
+        for layer in stack:
+            for xg, xq, xs, xsum, mats in layer["groups"]:
+                K = xg.shape[1]
+                xb = synth.tokens_bf16_torch(N, K, 13 + N)
+                q = bn.quant_act(xb)
+                for P, alpha, dot, y, M, _ in mats:
+                    d = torch.empty((N, M), dtype=torch.int32, device="cuda")
+                    yy = torch.empty((N, M), dtype=torch.float32, device="cuda")
+                    bufs.append((P, alpha, q, d, yy, M, K))
+
+        def run(bufs=bufs):
+            for P, alpha, q, d, yy, M, K in bufs:
+                bn.gemv(P, alpha, q[0], q[1], q[2], out=(d, yy))
+        g = capture(torch, run)
+        t = time_graph(torch, g, 10, 3) / 10
+        byts = sum(M * K // 4 + N * K + N * M * 8 for P, a, q, d, yy, M, K in bufs)
+        ops = sum(2 * M * K * N for P, a, q, d, yy, M, K in bufs)
+        rows[f"decode_N{N}"] = {"workload": "2B-class stack, 30 layers x 7 GEMVs",
+                                "us_per_step": round(t * 1e6, 1),
+                                "GB/s": round(byts / t / 1e9, 1),
+                                "TOPS": round(ops / t / 1e12, 3),
+                                "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs, g
+    # a3 at streaming sizes: large layer (8 layers x 7 projections, 1.71 GB), N = 1 and 16
+    large = []
+    for l in range(8):
+        for p in synth.PROJ_NAMES:
+            M, K = synth.SHAPES["large"][p]
+            W = synth.ternary_torch(M, K, synth.stack_seed("large", l, p, "weights"))
+            large.append((bn.pack(W), synth.weight_scale(synth.rng_for("large", l, p, "scale")), M, K))
+            del W
+    for N in (1, 16):
+        bufs = []
+        qs = {}
+        for P, alpha, M, K in large:
+            if K not in qs:
+                qs[K] = bn.quant_act(synth.tokens_bf16_torch(N, K, 17 + K))
+            q = qs[K]
+            bufs.append((P, alpha, q, torch.empty((N, M), dtype=torch.int32, device="cuda"),
+                         torch.empty((N, M), dtype=torch.float32, device="cuda"), M, K))
+
+        def run(bufs=bufs):
+            for P, alpha, q, d, yy, M, K in bufs:
+                bn.gemv(P, alpha, q[0], q[1], q[2], out=(d, yy))
+        g = capture(torch, run)
+        t = time_graph(torch, g, 5, 2) / 5
+        byts = sum(M * K // 4 + N * K + N * M * 8 for P, a, q, d, yy, M, K in bufs)
+        rows[f"large_N{N}"] = {"workload": "large layer stack, 8 layers x 7 GEMVs, 1.71 GB packed",
+                               "us_per_step": round(t * 1e6, 1),
+                               "GB/s": round(byts / t / 1e9, 1),
+                               "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+                               "tokens_per_s": round(N / t, 1)}
+        del bufs, g
+    del large
+    # a5: prefill GEMM on the 0.6B-class projections, N = 128 and 4096
+    e06 = []
+    for p in synth.PROJ_NAMES:
+        M, K = synth.SHAPES["e06"][p]
+        W = synth.ternary_torch(M, K, synth.stack_seed("e06", 0, p, "weights"))
+        e06.append((bn.pack(W), synth.weight_scale(synth.rng_for("e06", 0, p, "scale")), M, K))
+        del W
+    for N in (128, 4096):
+        for outputs in ("y", "dot+y"):
+            bufs = []
+            for P, alpha, M, K in e06:
+                q = bn.quant_act(synth.tokens_bf16_torch(N, K, 19 + K))
+                d = torch.empty((N, M), dtype=torch.int32, device="cuda") if outputs != "y" else None
+                yy = torch.empty((N, M), dtype=torch.float32, device="cuda")
+                bufs.append((P, alpha, q, d, yy, M, K))
+
+            def run(bufs=bufs, outputs=outputs):
+                for P, alpha, q, d, yy, M, K in bufs:
+                    bn.gemm(P, alpha, q[0], q[1], q[2], want_dot=d is not None, out=(d, yy))
+            t = _events_time(torch, run, 20)
+            ops = sum(2 * M * K * N for P, a, q, d, yy, M, K in bufs)
+            rows[f"prefill_N{N}_{outputs}"] = {
+                "workload": "0.6B-class q/k/v/o/gate/up/down", "us": round(t * 1e6, 1),
+                "TOPS": round(ops / t / 1e12, 2),
+                "mfma_frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)}
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -184,16 +315,17 @@ def main():
     el = time_graph(torch, g_step, args.steps, args.warmup)
     ms = el / args.steps * 1e3
     value = sbytes / (el / args.steps) / 1e9
+    launches = len(stack) * len(GROUPS)
+    # the dominant (and only) kernel of the step is the fused GEMV: its average
+    # launch duration is the step time over its launches (HIP events on the
+    # stream the graph runs on)
+    per_launch_s = el / (args.steps * launches)
+    achieved = sbytes / launches / per_launch_s / 1e9
 
-    # dominant kernel: the GEMV alone, same launches, its own graph and events
-    n_gemv = sum(len(g[4]) for layer in stack for g in layer["groups"])
-    g_gemv = capture(torch, lambda: run_step(bn, stack, quant=False))
-    el_g = time_graph(torch, g_gemv, args.steps, args.warmup)
-    per_launch_s = el_g / (args.steps * n_gemv)
-    gb = gemv_bytes(stack)
-    achieved = gb / n_gemv / per_launch_s / 1e9
-
-    # eager (no graph) step time, for context
+    # context: the same work through the unfused calls, in a graph, and eager
+    g_unf = capture(torch, lambda: run_step_unfused(bn, stack))
+    unfused_ms = time_graph(torch, g_unf, args.steps, args.warmup) / args.steps * 1e3
+    del g_unf
     run_step(bn, stack)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -202,6 +334,7 @@ def main():
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) / 5 * 1e3
 
+    rows = None if args.no_rows else secondary_rows(bn, synth, torch, stack)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     out = {
@@ -222,14 +355,16 @@ def main():
                    "packed_bytes_per_step": sum(m[0].numel() for layer in stack
                                                 for g in layer["groups"] for m in g[4]),
                    "algorithmic_bytes_per_step": sbytes,
-                   "launches_per_step": n_gemv + len(stack) * len(GROUPS),
+                   "launches_per_step": launches,
                    "graph": True,
-                   "eager_ms_per_step": round(eager_ms, 3)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_valu_kernel<1>",
+                   "eager_ms_per_step": round(eager_ms, 3),
+                   "unfused_graph_ms_per_step": round(unfused_ms, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_valu_kernel<1,PF,2> (fused bf16 quantise + GEMV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(per_launch_s * 1e6, 3)},
         "cpu_baseline": cpu,
+        "rows": rows,
     }
     print(json.dumps(out), flush=True)
 

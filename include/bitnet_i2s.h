@@ -42,9 +42,10 @@ extern "C" {
 #endif
 
 #define BITNET_ABI_VERSION 1
-#define BITNET_MAX_K 65536          /* largest supported reduction length   */
+#define BITNET_MAX_K 32768          /* largest supported reduction length   */
 #define BITNET_GEMV_MAX_N 64        /* largest token count of the decode call */
 #define BITNET_GEMM_MAX_N (1 << 21) /* largest token count of the prefill call */
+#define BITNET_MAX_GROUP 8          /* matrices per bitnet_linear_i2s call     */
 
 typedef enum {
     BITNET_OK = 0,
@@ -125,6 +126,38 @@ int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t M,
                        int64_t K, const int8_t *xq, const float *x_scale,
                        const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
                        void *stream);
+
+/*
+ * bitnet_linear_i2s -- fused decode linear: quantise tokens and multiply them
+ * by up to BITNET_MAX_GROUP I2_S matrices that share them, in one launch.
+ * [P1 §4-5 (per-token scale), §4-3 (a weight block reused for several
+ * activation columns); P2 §3; P3 §3.2]
+ *
+ *   x        [N][K] fp32 or bf16 tokens (as bitnet_quant_act_i8), 16-byte aligned.
+ *   mats     host array of n_mats descriptors, read during the call only:
+ *              packed [M][K/4] I2_S (16-byte aligned), M, w_scale, and the
+ *              outputs dot [N][M] int32 / y [N][M] fp32 (either may be NULL,
+ *              not both, unless M == 0).
+ *   xq, x_scale, x_sum   optional outputs (may be NULL when N <= 8): the
+ *              quantised tokens exactly as bitnet_quant_act_i8 writes them.
+ *              Required when N > 8 (they then carry the tokens between the
+ *              quantiser and the MFMA kernel).
+ *
+ * Every output equals what bitnet_quant_act_i8 followed by
+ * bitnet_gemv_i2s_i8 on each matrix produces, bit for bit.
+ * 0 <= N <= BITNET_GEMV_MAX_N; 1 <= n_mats <= BITNET_MAX_GROUP.
+ */
+typedef struct {
+    const uint8_t *packed;
+    int64_t M;
+    float w_scale;
+    int32_t *dot;
+    float *y;
+} bitnet_i2s_matrix;
+
+int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
+                      const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq,
+                      float *x_scale, int32_t *x_sum, void *stream);
 
 /* Thread-local description of the last non-OK status on this thread
  * (empty string if none).  The pointer stays valid until the next call on

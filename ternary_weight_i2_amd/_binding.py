@@ -18,6 +18,16 @@ F32, BF16 = 0, 1
 GEMV_MAX_N = 64
 
 
+MAX_GROUP = 8
+
+
+class I2SMatrix(ctypes.Structure):
+    """Mirror of bitnet_i2s_matrix."""
+    _fields_ = [("packed", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("w_scale", ctypes.c_float), ("dot", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
+
+
 class BitnetError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"bitnet status {status}: {msg}")
@@ -47,6 +57,9 @@ def load() -> ctypes.CDLL:
     sig = [p, f32, i64, i64, p, p, p, i64, p, p, p]
     L.bitnet_gemv_i2s_i8.argtypes = sig
     L.bitnet_gemm_i2s_i8.argtypes = sig
+    L.bitnet_linear_i2s.argtypes = [p, ctypes.c_int, i64, i64, ctypes.POINTER(I2SMatrix),
+                                    ctypes.c_int, p, p, p, p]
+    L.bitnet_linear_i2s.restype = ctypes.c_int
     for fn in ("bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
                "bitnet_gemm_i2s_i8", "bitnet_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
@@ -139,3 +152,35 @@ def gemm(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=No
     K = xq.shape[1]
     return _matmul(load().bitnet_gemm_i2s_i8, packed, w_scale, K, xq, x_scale,
                    x_sum, want_dot, want_y, out)
+
+
+def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
+    """Fused decode linear: quantise tokens x[N][K] (fp32/bf16, cuda) and multiply
+    them by every (packed, w_scale) in ``mats`` in one launch (N <= 8; for
+    N > 8 the library quantises into ``qout`` first, allocated here if None).
+
+    Returns ([(dot | None, y | None) per matrix], (xq, s, xsum) | None)."""
+    import torch
+    if x.dim() != 2:
+        raise TypeError("x must be 2-D [N][K]")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError("x must be float32 or bfloat16")
+    N, K = x.shape
+    if out is None:
+        out = []
+        for P, _ in mats:
+            M = P.shape[0]
+            out.append((torch.empty((N, M), dtype=torch.int32, device=x.device) if want_dot else None,
+                        torch.empty((N, M), dtype=torch.float32, device=x.device) if want_y else None))
+    if qout is None and N > 8:
+        qout = (torch.empty((N, K), dtype=torch.int8, device=x.device),
+                torch.empty((N,), dtype=torch.float32, device=x.device),
+                torch.empty((N,), dtype=torch.int32, device=x.device))
+    arr = (I2SMatrix * len(mats))()
+    for i, ((P, ws), (d, y)) in enumerate(zip(mats, out)):
+        arr[i] = I2SMatrix(_ptr(P), P.shape[0], float(ws), _ptr(d), _ptr(y))
+    xq, xs, xsum = qout if qout is not None else (None, None, None)
+    _check(load().bitnet_linear_i2s(_ptr(x), dt, N, K, arr, len(mats), _ptr(xq), _ptr(xs),
+                                    _ptr(xsum), _stream(x)))
+    return out, qout

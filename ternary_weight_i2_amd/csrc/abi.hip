@@ -152,10 +152,14 @@ BITNET_API int bitnet_gemv_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
         return s;
     if (M == 0 || N == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = N <= 8 ? bitnet::launch_gemv_valu(packed, w_scale, M, K, xq, x_scale, x_sum,
-                                                     N, dot, y, st)
-                          : bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum,
-                                                     N, dot, y, st);
+    hipError_t e;
+    if (N <= 8) {
+        bitnet::GemvMat m{packed, dot, y, w_scale, (int)M, 0};
+        e = bitnet::launch_gemv_valu(&m, 1, K, N, 0, xq, x_scale, x_sum, nullptr, nullptr,
+                                     nullptr, st);
+    } else {
+        e = bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot, y, st);
+    }
     if (e != hipSuccess) return hip_fail("bitnet_gemv_i2s_i8: launch", e);
     return ok();
 }
@@ -171,5 +175,58 @@ BITNET_API int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
     hipError_t e = bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot,
                                             y, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("bitnet_gemm_i2s_i8: launch", e);
+    return ok();
+}
+
+BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
+                                 const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq,
+                                 float *x_scale, int32_t *x_sum, void *stream) {
+    const char *fn = "bitnet_linear_i2s";
+    if (dtype != BITNET_F32 && dtype != BITNET_BF16)
+        return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (N < 0 || N > BITNET_GEMV_MAX_N)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld outside [0, %d]", fn, (long long)N,
+                    BITNET_GEMV_MAX_N);
+    if (int s = check_k(fn, K)) return s;
+    if (n_mats < 1 || n_mats > BITNET_MAX_GROUP)
+        return fail(BITNET_E_SHAPE, "%s: n_mats=%d outside [1, %d]", fn, n_mats,
+                    BITNET_MAX_GROUP);
+    if (!mats) return fail(BITNET_E_NULL, "%s: mats is NULL", fn);
+    bitnet::GemvMat gm[bitnet::kMaxMats];
+    for (int i = 0; i < n_mats; ++i) {
+        const bitnet_i2s_matrix &m = mats[i];
+        if (m.M < 0 || m.M > 0x7fffffffLL)
+            return fail(BITNET_E_SHAPE, "%s: mats[%d].M=%lld out of range", fn, i, (long long)m.M);
+        if (m.M > 0) {
+            if (!m.packed) return fail(BITNET_E_NULL, "%s: mats[%d].packed is NULL", fn, i);
+            if (!m.dot && !m.y)
+                return fail(BITNET_E_NULL, "%s: mats[%d] has neither dot nor y", fn, i);
+            if (!aligned(m.packed, 16))
+                return fail(BITNET_E_ALIGN, "%s: mats[%d].packed must be 16-byte aligned", fn, i);
+            if ((m.dot && !aligned(m.dot, 4)) || (m.y && !aligned(m.y, 4)))
+                return fail(BITNET_E_ALIGN, "%s: mats[%d] outputs must be 4-byte aligned", fn, i);
+        }
+        gm[i] = bitnet::GemvMat{m.packed, m.dot, m.y, m.w_scale, (int)m.M, 0};
+    }
+    if (N == 0) return ok();
+    if (!x) return fail(BITNET_E_NULL, "%s: x is NULL", fn);
+    if (!aligned(x, 16) || (xq && !aligned(xq, 16)) || (x_scale && !aligned(x_scale, 4)) ||
+        (x_sum && !aligned(x_sum, 4)))
+        return fail(BITNET_E_ALIGN, "%s: x/xq must be 16-byte and x_scale/x_sum 4-byte aligned", fn);
+    if (N > 8 && (!xq || !x_scale || !x_sum))
+        return fail(BITNET_E_NULL, "%s: N > 8 needs the xq, x_scale and x_sum buffers", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (N <= 8) {
+        e = bitnet::launch_gemv_valu(gm, n_mats, K, N, dtype == BITNET_BF16 ? 2 : 1, x, nullptr,
+                                     nullptr, xq, x_scale, x_sum, st);
+    } else {
+        e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
+        for (int i = 0; i < n_mats && e == hipSuccess; ++i)
+            if (gm[i].M > 0)
+                e = bitnet::launch_gemm_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
+                                             x_sum, N, gm[i].dot, gm[i].y, st);
+    }
+    if (e != hipSuccess) return hip_fail("bitnet_linear_i2s: launch", e);
     return ok();
 }

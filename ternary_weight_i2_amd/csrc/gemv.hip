@@ -1,137 +1,400 @@
-// gemv.hip -- decode matmul for 1..8 tokens on the vector ALUs.
+// gemv.hip -- decode matmul (a few tokens) on the vector ALUs.
 //
 // Pages: [P2] "[분석/검증-3] BitNet.cpp ARM 커널 재작성" §3 and [P3] "[기술 분석
 // 보고서] ARM64 ... 1.58-bit ..." §3.1-§4 (raw codes 0/1/2 multiply the
 // activations at offsets k, k+32, k+64, k+96 of a block; the scale is applied
-// by the caller); [P1] "BitNet 딥다이브" §4-3 (a weight block is loaded once
-// and reused for several activation columns).
+// by the caller); [P1] "BitNet 딥다이브" §2-1 (decode is bound by reading the
+// weights), §4-3 (a weight block is loaded once and reused for several
+// activation columns), §4-5 (per-token activation scale).
 //
-// Design (gfx950, wave64): one wave owns one output row at a time and walks
-// the packed row with 16-byte loads, lane c taking chunk c, c+64, ...
-// A 16-byte chunk is half an I2_S block: dword j holds block bytes
-// g0+4j..g0+4j+3 and therefore the codes of positions g0+4j+e+32*i.  Masking
-// a dword keeps one 2-bit field per byte, which v_dot4_i32_i8 multiplies
-// straight against four contiguous int8 activations:
-//   field i=3 (bits 1-0): w & 0x03030303       -> code * 1
-//   field i=2 (bits 3-2): w & 0x0C0C0C0C       -> code * 4
-//   field i=1 (bits 5-4): w & 0x30303030       -> code * 16
+// Work split (gfx950, wave64): a workgroup of 4 waves owns `rows_per_wg`
+// consecutive rows of one matrix, walked in row groups (see the kernel).  A
+// row is read as 16-byte chunks (coalesced dwordx4 loads, each packed byte
+// fetched exactly once).  A 16-byte chunk c is
+// half an I2_S block (b = c/2, half h = c%2): dword j holds block bytes
+// 16h+4j..16h+4j+3 and so the codes of positions 32i + 16h + 4j + e.
+// Masking a dword keeps one 2-bit field per byte and v_dot4_i32_i8 multiplies
+// it with four contiguous int8 activations:
+//   field i=3 (bits 1-0): w & 0x03030303        -> code * 1
+//   field i=2 (bits 3-2): w & 0x0C0C0C0C        -> code * 4
+//   field i=1 (bits 5-4): w & 0x30303030        -> code * 16
 //   field i=0 (bits 7-6): (w >> 2) & 0x30303030 -> code * 16
-// so three accumulators (x1, x4, x16) need no per-field shifts; their exact
-// combination acc1 + acc4/4 + acc16/16 is the raw-code sum R, and the exact
-// dot is D = R - sum(x).  Tokens are staged in LDS once per workgroup and
-// every weight chunk is reused for all tokens of the call.
+// Three accumulators (x1, x4, x16) avoid per-field shifts; acc1 + acc4/4 +
+// acc16/16 is the raw-code sum R exactly, and D = R - sum(x).
+//
+// Activations live in LDS in a group-major layout: token t, field i, chunk c
+// at byte t*K + i*(K/4) + 16c holds x[128*(c/2) + 32i + 16*(c%2) + 0..15],
+// so the four 16-byte reads a lane makes per chunk are contiguous across the
+// wave (no bank conflicts).  Before the activations are staged, each wave has
+// already issued the loads of its first row group, so the two memory
+// latencies overlap; afterwards every row group's loads are issued one group
+// ahead of its arithmetic.
+//
+// Modes: 0 = int8 xq (+ scale and sum) from global memory; 1/2 = fp32/bf16
+// tokens quantised in the prologue with the same arithmetic as the
+// stand-alone quantiser (every workgroup recomputes the identical values;
+// workgroup 0 optionally stores them).  One launch may serve up to kMaxMats
+// matrices that share the tokens (e.g. q/k/v, or gate/up).
 #include "common.h"
 
 namespace bitnet {
 
 constexpr int kGemvThreads = 256;
-constexpr int kLdsBytes = 65536;   // activation staging budget per workgroup
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kLdsBytes = 61440;   // activation staging budget per workgroup (60 KiB)
 
-template <int NT>
-__global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(
-    const uint8_t *__restrict__ packed, float alpha, int M, int K,
-    const int8_t *__restrict__ xq, const float *__restrict__ xs,
-    const int32_t *__restrict__ xsum, int ntok, int32_t *__restrict__ dot,
-    float *__restrict__ y, int rows_per_wg) {
+template <int MODE>
+struct TokVec;   // 16 bytes of a token row, widened to fp32
+template <>
+struct TokVec<1> {
+    static constexpr int kElems = 4;
+    __device__ static void load(const char *row, int q, float *v) {
+        const float4 f = reinterpret_cast<const float4 *>(row)[q];
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+};
+template <>
+struct TokVec<2> {
+    static constexpr int kElems = 8;
+    __device__ static void load(const char *row, int q, float *v) {
+        const uint4 u = reinterpret_cast<const uint4 *>(row)[q];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(w[j] << 16);
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+};
+
+// LDS byte offset of activation element k of token t (group-major layout)
+__device__ __forceinline__ int lds_pos(int t, int K, int k) {
+    const int b = k >> 7, i = (k >> 5) & 3, h = (k >> 4) & 1, e = k & 15;
+    return t * K + i * (K >> 2) + 32 * b + 16 * h + e;
+}
+
+// Quantise ntok tokens of x (fp32 or bf16) into LDS; per-token s and sum
+// land in s_tok / sum_tok.  Workgroup 0 also writes the optional outputs.
+// Each thread keeps up to XR 16-byte pieces of a token in registers between
+// the absmax pass and the quantise pass; longer tokens are re-read (L1/L2).
+template <int NT, int MODE>
+__device__ void quantise_prologue(const GemvArgs &a, int8_t *xl, float *s_tok,
+                                  int *sum_tok, float (*redf)[NT], int (*redi)[NT]) {
+    using V = TokVec<MODE>;
+    constexpr int E = V::kElems;
+    constexpr int XR = NT == 1 ? 4 : (NT == 2 ? 2 : 1);   // register budget
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int K = a.K, nq = K / E;
+    const bool keep = NT <= 2 && nq <= XR * kGemvThreads;
+    const char *x = reinterpret_cast<const char *>(a.x);
+    const int rowb = K * (MODE == 2 ? 2 : 4);
+    float am[NT];
+    float reg[NT][XR][E];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        am[t] = 0.0f;
+        if (t < a.ntok) {
+            if (keep) {
+#pragma unroll
+                for (int r = 0; r < XR; ++r) {
+                    const int q = tid + r * kGemvThreads;
+                    if (q < nq) {
+                        V::load(x + t * rowb, q, reg[t][r]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) am[t] = fmaxf(am[t], fabsf(reg[t][r][e]));
+                    }
+                }
+            } else {
+                for (int q = tid; q < nq; q += kGemvThreads) {
+                    float v[E];
+                    V::load(x + t * rowb, q, v);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) am[t] = fmaxf(am[t], fabsf(v[e]));
+                }
+            }
+        }
+        am[t] = wave_max_f32(am[t]);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) redf[wv][t] = am[t];
+    }
+    __syncthreads();
+    float s[NT];
+    int sm[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        s[t] = quant_scale(fmaxf(fmaxf(redf[0][t], redf[1][t]), fmaxf(redf[2][t], redf[3][t])));
+        sm[t] = 0;
+    }
+    const bool store = blockIdx.x == 0 && a.xq_out != nullptr;
+    auto emit = [&](int t, int q, const float *v) {
+        uint32_t pq[E / 4];
+#pragma unroll
+        for (int j = 0; j < E / 4; ++j) pq[j] = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int qi = quant_one(v[e], s[t]);
+            sm[t] += qi;
+            pq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+        }
+        const int pos = lds_pos(t, K, q * E);
+        if constexpr (E == 8) {
+            const uint2 u = make_uint2(pq[0], pq[E / 4 - 1]);
+            *reinterpret_cast<uint2 *>(xl + pos) = u;
+            if (store) reinterpret_cast<uint2 *>(a.xq_out + (int64_t)t * K)[q] = u;
+        } else {
+            *reinterpret_cast<uint32_t *>(xl + pos) = pq[0];
+            if (store) reinterpret_cast<uint32_t *>(a.xq_out + (int64_t)t * K)[q] = pq[0];
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t < a.ntok) {
+            if (keep) {
+#pragma unroll
+                for (int r = 0; r < XR; ++r) {
+                    const int q = tid + r * kGemvThreads;
+                    if (q < nq) emit(t, q, reg[t][r]);
+                }
+            } else {
+                for (int q = tid; q < nq; q += kGemvThreads) {
+                    float v[E];
+                    V::load(x + t * rowb, q, v);
+                    emit(t, q, v);
+                }
+            }
+        }
+        sm[t] = wave_sum_i32(sm[t]);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) redi[wv][t] = sm[t];
+    }
+    __syncthreads();
+    if (tid < NT && tid < a.ntok) {
+        const int total = redi[0][tid] + redi[1][tid] + redi[2][tid] + redi[3][tid];
+        s_tok[tid] = s[tid];
+        sum_tok[tid] = total;
+        if (blockIdx.x == 0) {
+            if (a.xs_out) a.xs_out[tid] = s[tid];
+            if (a.xsum_out) a.xsum_out[tid] = total;
+        }
+    }
+}
+
+// Work split: a wave handles row groups of 64/LPR rows, LPR lanes per row;
+// lane u of a row takes the row's 16-byte chunks u, u+LPR, ..., at most JM of
+// them (J = ceil(C/LPR) at run time).  The host picks LPR so that J <= JM and
+// few lanes idle (K=2560: 8 lanes x 5 chunks; K=6912: 16 x 7; K=8192: 16 x 8;
+// K=28672: 64 x 7).  All J loads of a row group are in flight together, and
+// the next row group's loads are issued before the current one is used.
+template <int NT, int LPR, int MODE>
+__global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs a) {
+    constexpr int JM = 8;
+    constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
-    const int8_t *xl = reinterpret_cast<const int8_t *>(lds);
-    {
-        const int n16 = ntok * (K / 16);
-        const int4 *src = reinterpret_cast<const int4 *>(xq);
-        for (int i = threadIdx.x; i < n16; i += kGemvThreads) lds[i] = src[i];
+    int8_t *xl = reinterpret_cast<int8_t *>(lds);
+    __shared__ float s_tok[NT];
+    __shared__ int sum_tok[NT];
+    __shared__ float redf[kGemvWaves][NT];
+    __shared__ int redi[kGemvWaves][NT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int sub = lane / LPR, u = lane % LPR;
+    int mi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+        if (i < a.nmats && (int)blockIdx.x >= a.mat[i].wg_begin) mi = i;
+    const uint8_t *packed = a.mat[mi].packed;
+    const int M = a.mat[mi].M;
+    const int K = a.K;
+    const int C = K >> 6;                       // 16-byte chunks per packed row
+    const int J = (C + LPR - 1) / LPR;
+    const int row0 = ((int)blockIdx.x - a.mat[mi].wg_begin) * a.rows_per_wg;
+    const int row1 = min(M, row0 + a.rows_per_wg);
+    // row groups of this wave: rows row0 + (g*4 + wv)*RG + sub
+    const int ngroups = (row1 - row0 + RG * kGemvWaves - 1) / (RG * kGemvWaves);
+    const int4 zero4 = make_int4(0, 0, 0, 0);
+
+    int4 cur[JM], nxt[JM];
+    auto load_group = [&](int g, int4 *r) {
+        const int row = row0 + (g * kGemvWaves + wv) * RG + sub;
+        const v4i *prow = reinterpret_cast<const v4i *>(packed + (int64_t)row * (K >> 2));
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int c = u + LPR * j;
+            if (j < J && c < C && row < row1) {
+                const v4i v = __builtin_nontemporal_load(prow + c);
+                r[j] = make_int4(v.x, v.y, v.z, v.w);
+            } else {
+                r[j] = zero4;
+            }
+        }
+    };
+    if (ngroups > 0) load_group(0, cur);
+
+    // ---- activations -> LDS (group-major), per-token scale and sum ----
+    if constexpr (MODE == 0) {
+        const int n16 = a.ntok * (K >> 4);
+        const int4 *src = reinterpret_cast<const int4 *>(a.x);
+        for (int q = tid; q < n16; q += kGemvThreads) {
+            const int t = q / (K >> 4), k = (q - t * (K >> 4)) << 4;
+            *reinterpret_cast<int4 *>(xl + lds_pos(t, K, k)) = src[q];
+        }
+        if (tid < NT && tid < a.ntok) {
+            s_tok[tid] = a.xs_in[tid];
+            sum_tok[tid] = a.xsum_in[tid];
+        }
+    } else {
+        quantise_prologue<NT, MODE>(a, xl, s_tok, sum_tok, redf, redi);
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int C = K >> 6;   // 16-byte chunks per packed row
-    const int row0 = blockIdx.x * rows_per_wg;
-    const int row1 = min(M, row0 + rows_per_wg);
-    for (int row = row0 + wv; row < row1; row += kGemvThreads / 64) {
+    const int gstride = K >> 2;   // bytes between fields in LDS
+    int32_t *dot = a.mat[mi].dot;
+    float *y = a.mat[mi].y;
+    const float alpha = a.mat[mi].alpha;
+    for (int g = 0; g < ngroups; ++g) {
+        if (g + 1 < ngroups) load_group(g + 1, nxt);
         int a1[NT], a4[NT], a16[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) a1[t] = a4[t] = a16[t] = 0;
-        const int4 *prow = reinterpret_cast<const int4 *>(packed + (int64_t)row * (K >> 2));
-        for (int c = lane; c < C; c += 64) {
-            const v4i pv = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(prow) + c);
-            const int4 p = make_int4(pv.x, pv.y, pv.z, pv.w);
-            const int xoff = (c >> 1) * kBlock + (c & 1) * 16;
-            const int pw[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t < ntok) {
-                    const int8_t *xt = xl + t * K + xoff;
-                    const int4 x0 = *reinterpret_cast<const int4 *>(xt);
-                    const int4 x1 = *reinterpret_cast<const int4 *>(xt + 32);
-                    const int4 x2 = *reinterpret_cast<const int4 *>(xt + 64);
-                    const int4 x3 = *reinterpret_cast<const int4 *>(xt + 96);
-                    const int xv0[4] = {x0.x, x0.y, x0.z, x0.w};
-                    const int xv1[4] = {x1.x, x1.y, x1.z, x1.w};
-                    const int xv2[4] = {x2.x, x2.y, x2.z, x2.w};
-                    const int xv3[4] = {x3.x, x3.y, x3.z, x3.w};
+        for (int j = 0; j < JM; ++j) {
+            const int c = u + LPR * j;
+            if (j < J && c < C) {
+                const int pw[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        a16[t] = dot4((pw[j] >> 2) & 0x30303030, xv0[j], a16[t]);
-                        a16[t] = dot4(pw[j] & 0x30303030, xv1[j], a16[t]);
-                        a4[t] = dot4(pw[j] & 0x0C0C0C0C, xv2[j], a4[t]);
-                        a1[t] = dot4(pw[j] & 0x03030303, xv3[j], a1[t]);
+                for (int t = 0; t < NT; ++t) {
+                    if (t < a.ntok) {
+                        const int8_t *xt = xl + t * K + 16 * c;
+                        const int4 x0 = *reinterpret_cast<const int4 *>(xt);
+                        const int4 x1 = *reinterpret_cast<const int4 *>(xt + gstride);
+                        const int4 x2 = *reinterpret_cast<const int4 *>(xt + 2 * gstride);
+                        const int4 x3 = *reinterpret_cast<const int4 *>(xt + 3 * gstride);
+                        const int xv0[4] = {x0.x, x0.y, x0.z, x0.w};
+                        const int xv1[4] = {x1.x, x1.y, x1.z, x1.w};
+                        const int xv2[4] = {x2.x, x2.y, x2.z, x2.w};
+                        const int xv3[4] = {x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            a16[t] = dot4((pw[d] >> 2) & 0x30303030, xv0[d], a16[t]);
+                            a16[t] = dot4(pw[d] & 0x30303030, xv1[d], a16[t]);
+                            a4[t] = dot4(pw[d] & 0x0C0C0C0C, xv2[d], a4[t]);
+                            a1[t] = dot4(pw[d] & 0x03030303, xv3[d], a1[t]);
+                        }
                     }
                 }
             }
         }
+        const int row = row0 + (g * kGemvWaves + wv) * RG + sub;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (t < ntok) {
+            if (t < a.ntok) {
                 // a4 and a16 are exact multiples of 4 and 16
                 int r = a1[t] + (a4[t] >> 2) + (a16[t] >> 4);
-                r = wave_sum_i32(r);
-                if (lane == t) {
-                    const int d = r - xsum[t];
+#pragma unroll
+                for (int o = LPR / 2; o > 0; o >>= 1) r += __shfl_xor(r, o, 64);
+                if (u == t && row < row1) {
+                    const int d = r - sum_tok[t];
                     if (dot) dot[(int64_t)t * M + row] = d;
-                    if (y) y[(int64_t)t * M + row] = ((float)d * alpha) / xs[t];
+                    if (y) y[(int64_t)t * M + row] = ((float)d * alpha) / s_tok[t];
                 }
             }
         }
+#pragma unroll
+        for (int j = 0; j < JM; ++j) cur[j] = nxt[j];
     }
 }
 
-template <int NT>
-static hipError_t run_gemv(const uint8_t *packed, float alpha, int64_t M, int64_t K,
-                           const int8_t *xq, const float *xs, const int32_t *xsum,
-                           int ntok, int32_t *dot, float *y, hipStream_t st) {
-    // rows per workgroup: aim for >= 4 workgroups per CU on a 256-CU part
-    int rows_per_wg = 4;
-    while (rows_per_wg < 64 && (M + rows_per_wg * 2 - 1) / (rows_per_wg * 2) >= 1024)
-        rows_per_wg *= 2;
-    const unsigned grid = (unsigned)((M + rows_per_wg - 1) / rows_per_wg);
-    const size_t lds = (size_t)ntok * (size_t)K;
-    hipLaunchKernelGGL(gemv_valu_kernel<NT>, dim3(grid), dim3(kGemvThreads), lds, st,
-                       packed, alpha, (int)M, (int)K, xq, xs, xsum, ntok, dot, y,
-                       rows_per_wg);
+template <int NT, int LPR>
+static hipError_t launch_nt_lpr(const GemvArgs &a, int mode, unsigned grid, hipStream_t st) {
+    const size_t lds = (size_t)a.ntok * (size_t)a.K;
+    if (mode == 0)
+        hipLaunchKernelGGL((gemv_valu_kernel<NT, LPR, 0>), dim3(grid), dim3(kGemvThreads), lds, st, a);
+    else if (mode == 1)
+        hipLaunchKernelGGL((gemv_valu_kernel<NT, LPR, 1>), dim3(grid), dim3(kGemvThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((gemv_valu_kernel<NT, LPR, 2>), dim3(grid), dim3(kGemvThreads), lds, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_valu(const uint8_t *packed, float alpha, int64_t M,
-                            int64_t K, const int8_t *xq, const float *xs,
-                            const int32_t *xsum, int64_t N, int32_t *dot,
-                            float *y, hipStream_t st) {
-    // tokens per pass: as many as fit in the LDS budget, at most 8
+// lanes per row: the power of two in {8,16,32,64} with ceil(C/LPR) <= 8
+// chunks per lane that leaves the fewest lanes idle (ties: fewer lanes, i.e.
+// more rows per wave)
+static int pick_lpr(int C) {
+    int best = 64;
+    double best_eff = -1.0;
+    for (int l = 8; l <= 64; l *= 2) {
+        const int j = (C + l - 1) / l;
+        if (j > 8) continue;
+        const double eff = (double)C / (double)(l * j);
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = l;
+        }
+    }
+    return best;
+}
+
+template <int NT>
+static hipError_t launch_nt(const GemvArgs &a, int mode, int lpr, unsigned grid, hipStream_t st) {
+    switch (lpr) {
+        case 8: return launch_nt_lpr<NT, 8>(a, mode, grid, st);
+        case 16: return launch_nt_lpr<NT, 16>(a, mode, grid, st);
+        case 32: return launch_nt_lpr<NT, 32>(a, mode, grid, st);
+        default: return launch_nt_lpr<NT, 64>(a, mode, grid, st);
+    }
+}
+
+hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N,
+                            int mode, const void *x, const float *xs,
+                            const int32_t *xsum, int8_t *xq_out, float *xs_out,
+                            int32_t *xsum_out, hipStream_t st) {
+    const int C = (int)(K >> 6);
+    const int lpr = pick_lpr(C);
+    const int rows_per_iter = kGemvWaves * (64 / lpr);   // rows per workgroup row-group step
+    // Row groups per workgroup: one (every load in flight at once, a single
+    // scheduling round) unless that would need more than ~1024 workgroups.
+    int64_t total_rows = 0;
+    for (int i = 0; i < nmats; ++i) total_rows += mats[i].M;
+    int64_t iters = (total_rows + (int64_t)rows_per_iter * 1024 - 1) / ((int64_t)rows_per_iter * 1024);
+    if (iters < 1) iters = 1;
+    const int rows_per_wg = (int)(rows_per_iter * iters);
+    const int esize = mode == 0 ? 1 : (mode == 1 ? 4 : 2);
     int per = (int)(kLdsBytes / K);
     if (per > 8) per = 8;
     for (int64_t n0 = 0; n0 < N; n0 += per) {
         const int nt = (int)((N - n0) < per ? (N - n0) : per);
-        const int8_t *xq_n = xq + n0 * K;
-        int32_t *dot_n = dot ? dot + n0 * M : nullptr;
-        float *y_n = y ? y + n0 * M : nullptr;
+        GemvArgs a{};
+        int wg = 0;
+        for (int i = 0; i < nmats; ++i) {
+            a.mat[i] = mats[i];
+            a.mat[i].wg_begin = wg;
+            if (mats[i].dot) a.mat[i].dot = mats[i].dot + n0 * mats[i].M;
+            if (mats[i].y) a.mat[i].y = mats[i].y + n0 * mats[i].M;
+            wg += (mats[i].M + rows_per_wg - 1) / rows_per_wg;
+        }
+        a.nmats = nmats;
+        a.K = (int)K;
+        a.ntok = nt;
+        a.rows_per_wg = rows_per_wg;
+        a.x = reinterpret_cast<const char *>(x) + n0 * K * esize;
+        if (mode == 0) {
+            a.xs_in = xs + n0;
+            a.xsum_in = xsum + n0;
+        } else {
+            a.xq_out = xq_out ? xq_out + n0 * K : nullptr;
+            a.xs_out = xs_out ? xs_out + n0 : nullptr;
+            a.xsum_out = xsum_out ? xsum_out + n0 : nullptr;
+        }
+        if (wg == 0) continue;
         hipError_t e;
-        if (nt == 1)
-            e = run_gemv<1>(packed, alpha, M, K, xq_n, xs + n0, xsum + n0, nt, dot_n, y_n, st);
-        else if (nt == 2)
-            e = run_gemv<2>(packed, alpha, M, K, xq_n, xs + n0, xsum + n0, nt, dot_n, y_n, st);
-        else if (nt <= 4)
-            e = run_gemv<4>(packed, alpha, M, K, xq_n, xs + n0, xsum + n0, nt, dot_n, y_n, st);
-        else
-            e = run_gemv<8>(packed, alpha, M, K, xq_n, xs + n0, xsum + n0, nt, dot_n, y_n, st);
+        if (nt == 1) e = launch_nt<1>(a, mode, lpr, (unsigned)wg, st);
+        else if (nt == 2) e = launch_nt<2>(a, mode, lpr, (unsigned)wg, st);
+        else if (nt <= 4) e = launch_nt<4>(a, mode, lpr, (unsigned)wg, st);
+        else e = launch_nt<8>(a, mode, lpr, (unsigned)wg, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

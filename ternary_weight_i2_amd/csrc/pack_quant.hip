@@ -114,8 +114,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     if (lane == 0) red_f[wv] = a;
     __syncthreads();
     a = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
-    const float denom = a > 1e-5f ? a : 1e-5f;
-    const float s = (float)(127.0 / (double)denom);
+    const float s = quant_scale(a);
 
     int8_t *qrow = xq + n * K;
     int sum = 0;
@@ -127,9 +126,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
         for (int j = 0; j < E / 4; ++j) packedq[j] = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            float r = __builtin_rintf(v[e] * s);
-            r = fminf(fmaxf(r, -128.0f), 127.0f);
-            const int qi = (int)r;
+            const int qi = quant_one(v[e], s);
             sum += qi;
             packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
         }

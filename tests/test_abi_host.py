@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = set(declared_functions())
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
-            "bitnet_gemm_i2s_i8", "bitnet_last_error", "bitnet_abi_version"} <= fns
+            "bitnet_gemm_i2s_i8", "bitnet_linear_i2s", "bitnet_last_error",
+            "bitnet_abi_version"} <= fns
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -57,7 +58,7 @@ def test_pack_validation(L):
     assert "multiple of 128" in _err(L)
     assert L.bitnet_pack_i2s(FAKE, -1, 128, FAKE, None) == E_SHAPE
     assert L.bitnet_pack_i2s(FAKE, 4, 0, FAKE, None) == E_SHAPE
-    assert L.bitnet_pack_i2s(FAKE, 4, 65536 + 128, FAKE, None) == E_SHAPE
+    assert L.bitnet_pack_i2s(FAKE, 4, 32768 + 128, FAKE, None) == E_SHAPE
     assert L.bitnet_pack_i2s(None, 4, 128, FAKE, None) == E_NULL
     assert L.bitnet_pack_i2s(FAKE, 4, 128, None, None) == E_NULL
     assert L.bitnet_pack_i2s(FAKE + 1, 4, 128, FAKE, None) == E_ALIGN
@@ -109,6 +110,43 @@ def test_matmul_validation(L, name, maxn):
     assert call(M=0, packed=None, xq=None) == OK
     assert call(N=0, packed=None, xq=None) == OK
     assert _err(L) == ""
+
+
+def test_linear_validation(L):
+    from ternary_weight_i2_amd._binding import I2SMatrix
+    f = L.bitnet_linear_i2s
+
+    def mats(*ms):
+        arr = (I2SMatrix * len(ms))()
+        for i, m in enumerate(ms):
+            arr[i] = m
+        return arr
+    good = I2SMatrix(FAKE, 64, 0.1, FAKE, FAKE)
+    g1 = mats(good)
+    assert f(FAKE, 5, 1, 256, g1, 1, None, None, None, None) == E_DTYPE
+    assert f(FAKE, 1, 65, 256, g1, 1, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, -1, 256, g1, 1, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, 1, 200, g1, 1, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, 1, 256, g1, 0, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, 1, 256, mats(*[good] * 9), 9, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, 1, 256, None, 1, None, None, None, None) == E_NULL
+    assert f(None, 1, 1, 256, g1, 1, None, None, None, None) == E_NULL
+    assert f(FAKE, 1, 1, 256, mats(I2SMatrix(None, 64, 0.1, FAKE, FAKE)), 1,
+             None, None, None, None) == E_NULL
+    assert f(FAKE, 1, 1, 256, mats(I2SMatrix(FAKE, 64, 0.1, None, None)), 1,
+             None, None, None, None) == E_NULL
+    assert f(FAKE, 1, 1, 256, mats(good, I2SMatrix(MIS, 64, 0.1, FAKE, FAKE)), 2,
+             None, None, None, None) == E_ALIGN
+    assert f(FAKE, 1, 1, 256, mats(I2SMatrix(FAKE, -3, 0.1, FAKE, FAKE)), 1,
+             None, None, None, None) == E_SHAPE
+    assert f(MIS, 1, 1, 256, g1, 1, None, None, None, None) == E_ALIGN
+    assert f(FAKE, 1, 1, 256, g1, 1, MIS, None, None, None) == E_ALIGN
+    # N > 8 needs the token buffers
+    assert f(FAKE, 1, 9, 256, g1, 1, None, None, None, None) == E_NULL
+    # N == 0 and matrices with M == 0 are no-ops
+    assert f(None, 1, 0, 256, g1, 1, None, None, None, None) == OK
+    assert f(None, 1, 0, 256, mats(I2SMatrix(None, 0, 0.1, None, None)), 1,
+             None, None, None, None) == OK
 
 
 def test_last_error_is_per_thread(L):

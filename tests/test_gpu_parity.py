@@ -116,7 +116,7 @@ def test_pack_rejects_non_ternary(bn):
 
 
 # ------------------------------------------------------------------ quant
-@pytest.mark.parametrize("N,K", [(1, 128), (3, 512), (17, 2560), (5, 6912), (2, 65536)])
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 512), (17, 2560), (5, 6912), (2, 32768)])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_quant_bit_exact(bn, N, K, act):
     rng = np.random.default_rng(N * 7 + K)
@@ -207,8 +207,8 @@ def test_special_weights(bn):
 
 
 def test_extreme_activations_max_k(bn):
-    # every activation at +-127 with K = 65536: the largest |D| the ABI allows
-    K, M, N = 65536, 8, 2
+    # every activation at +-127 with K = 32768: the largest |D| the ABI allows
+    K, M, N = 32768, 8, 2
     W = np.ones((M, K), dtype=np.int8)
     W[1::2] = -1
     x = np.full((N, K), 3.0, dtype=np.float32)
@@ -272,3 +272,84 @@ def test_large_layer_sampled(bn, proj, N):
     M, K = synth.SHAPES["large"][proj]
     rows = [(0, 48), (M // 2 + 5, 48), (M - 33, 33)]
     run_case(bn, M, K, N, "gemv", seed=N + 100 * len(proj), rows=rows)
+
+
+# ------------------------------------------------------ fused decode linear
+def make_x(rng, N, K, dtype, outliers=False):
+    if dtype == "f32":
+        x = synth.tokens_f32(rng, N, K)
+        return x, dev(x)
+    x = synth.tokens_bf16(rng, N, K, outliers=outliers)
+    return x, to_bf16_tensor(x)
+
+
+def run_linear(bn, Ms, K, N, dtype, seed, rows=None, outliers=False, check_unfused=True):
+    """Fused quantise + grouped GEMV vs the oracle and vs the unfused calls."""
+    rng = np.random.default_rng(seed)
+    Ws = [synth.ternary(rng, M, K) for M in Ms]
+    alphas = [synth.weight_scale(rng) for _ in Ms]
+    x, xg = make_x(rng, N, K, dtype, outliers)
+    Ps = [bn.pack(dev(W)) for W in Ws]
+    qbuf = (torch.empty((N, K), dtype=torch.int8, device="cuda"),
+            torch.empty((N,), dtype=torch.float32, device="cuda"),
+            torch.empty((N,), dtype=torch.int32, device="cuda"))
+    outs, _ = bn.linear(xg, list(zip(Ps, alphas)), qout=qbuf)
+    torch.cuda.synchronize()
+    q, s, qs = oracle.quant_act(x)
+    np.testing.assert_array_equal(qbuf[0].cpu().numpy(), q)
+    np.testing.assert_array_equal(qbuf[1].cpu().numpy().view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(qbuf[2].cpu().numpy(), qs)
+    if check_unfused:
+        xq, xs, xsum = bn.quant_act(xg)
+    for W, P, alpha, (d, y) in zip(Ws, Ps, alphas, outs):
+        M = W.shape[0]
+        dn, yn = d.cpu().numpy(), y.cpu().numpy()
+        if check_unfused and M > 0:
+            d2, y2 = bn.gemv(P, alpha, xq, xs, xsum)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(dn, d2.cpu().numpy())
+            np.testing.assert_array_equal(yn.view(np.uint32), y2.cpu().numpy().view(np.uint32))
+        for r0, nr in (rows if rows is not None else [(0, M)]):
+            if nr == 0:
+                continue
+            Pr, _ = oracle.pack_i2s(W[r0:r0 + nr])
+            D, _ = oracle.linear_i2s(Pr, K, q, s, alpha, nthreads=8, want_y=False)
+            np.testing.assert_array_equal(dn[:, r0:r0 + nr], D)
+            check_y(yn[:, r0:r0 + nr], D, alpha, s)
+
+
+LINEAR_CASES = [((7,), 128, 1, "f32"), ((64, 0, 17), 256, 2, "bf16"),
+                ((130, 33, 65), 384, 5, "bf16"), ((100,), 640, 8, "f32"),
+                ((70, 70), 896, 9, "bf16"), ((65,), 384, 64, "bf16"),
+                ((3, 5, 7, 9, 11, 13, 15, 17), 512, 3, "bf16"), ((40,), 32768, 2, "f32"),
+                ((300,), 8192, 8, "bf16"), ((129,), 28672, 3, "bf16")]
+
+
+@pytest.mark.parametrize("Ms,K,N,dtype", LINEAR_CASES)
+def test_linear_small(bn, Ms, K, N, dtype):
+    run_linear(bn, Ms, K, N, dtype, seed=sum(Ms) + K + N)
+
+
+@pytest.mark.parametrize("group", ["attn", "o", "ffn", "down"])
+def test_linear_b2_decode_groups(bn, group):
+    """The benchmark's launch configuration: one fused launch per dependency
+    group of the 2B-class layer, N=1, bf16 token, every row compared."""
+    projs = {"attn": ("q", "k", "v"), "o": ("o",), "ffn": ("gate", "up"), "down": ("down",)}[group]
+    Ms = [synth.SHAPES["b2"][p][0] for p in projs]
+    K = synth.SHAPES["b2"][projs[0]][1]
+    run_linear(bn, Ms, K, 1, "bf16", seed=len(group) * 7)
+
+
+@pytest.mark.parametrize("N", [1, 4, 16, 64])
+def test_linear_b2_sparse_batched(bn, N):
+    Ms = [synth.SHAPES["b2"][p][0] for p in ("gate", "up")]
+    run_linear(bn, Ms, 2560, N, "bf16", seed=100 + N, outliers=True)
+
+
+@pytest.mark.parametrize("projs", [("q", "k", "v"), ("gate",), ("down",)])
+def test_linear_large_sampled(bn, projs):
+    Ms = [synth.SHAPES["large"][p][0] for p in projs]
+    K = synth.SHAPES["large"][projs[0]][1]
+    M0 = min(Ms)
+    rows = [(0, 32), (M0 // 2 + 3, 32), (M0 - 17, 17)]
+    run_linear(bn, Ms, K, 1, "bf16", seed=K + len(projs), rows=rows, check_unfused=False)
