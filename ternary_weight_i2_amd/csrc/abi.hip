@@ -11,6 +11,10 @@
 
 #define BITNET_API extern "C" __attribute__((visibility("default")))
 
+#ifndef BITNET_VALU_MAX_N
+#define BITNET_VALU_MAX_N 2   // decode token counts served by the vector-ALU GEMV (MFMA above)
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -153,12 +157,12 @@ BITNET_API int bitnet_gemv_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
     if (M == 0 || N == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (N <= 8) {
+    if (N <= BITNET_VALU_MAX_N) {
         bitnet::GemvMat m{packed, dot, y, w_scale, (int)M, 0};
         e = bitnet::launch_gemv_valu(&m, 1, K, N, 0, xq, x_scale, x_sum, nullptr, nullptr,
                                      nullptr, st);
     } else {
-        e = bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot, y, st);
+        e = bitnet::launch_gemv_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot, y, st);
     }
     if (e != hipSuccess) return hip_fail("bitnet_gemv_i2s_i8: launch", e);
     return ok();
@@ -224,7 +228,7 @@ BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
         e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
         for (int i = 0; i < n_mats && e == hipSuccess; ++i)
             if (gm[i].M > 0)
-                e = bitnet::launch_gemm_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
+                e = bitnet::launch_gemv_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
                                              x_sum, N, gm[i].dot, gm[i].y, st);
     }
     if (e != hipSuccess) return hip_fail("bitnet_linear_i2s: launch", e);

@@ -83,6 +83,10 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
                             int mode, const void *x, const float *xs,
                             const int32_t *xsum, int8_t *xq_out, float *xs_out,
                             int32_t *xsum_out, hipStream_t st);
+// Batched decode (1..64 tokens) on MFMA, weights streamed once.
+hipError_t launch_gemv_mfma(const uint8_t *packed, float alpha, int64_t M, int64_t K,
+                            const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                            int32_t *dot, float *y, hipStream_t st);
 hipError_t launch_gemm_mfma(const uint8_t *packed, float alpha, int64_t M,
                             int64_t K, const int8_t *xq, const float *xs,
                             const int32_t *xsum, int64_t N, int32_t *dot,

@@ -1,0 +1,182 @@
+// gemv_mfma.hip -- batched decode matmul (up to 64 tokens) on int8 MFMA.
+//
+// Pages: [P1] "BitNet 딥다이브" §2-1 (decode is bound by reading the weights),
+// §4-3 (a weight block is loaded once and reused for several activation
+// columns); [P2] "[분석/검증-3]" §3 and [P3] "[기술 분석 보고서]" §3.2 (raw codes
+// multiply the activations; the exact result subtracts sum(x)).
+//
+// At 8..64 tokens every packed byte feeds 64..512 int8 operations, more than
+// the vector ALUs sustain at HBM speed, so the contraction runs on
+// v_mfma_i32_16x16x64_i8 while the weights still stream from HBM once.
+//
+// Work split: a workgroup owns BM = 16*MI rows and all N tokens (NJ 16-token
+// tiles) over the full K, which its WAVES waves split into contiguous block
+// ranges.  Partial sums meet in LDS through exact integer adds (ds_add), so
+// no second pass and no global scratch is needed; the epilogue then writes
+// D = R - sum(x) and y = D * alpha / s.
+//
+// Operand layout: the B operand (tokens) is read in its natural row-major
+// order straight from global memory (the int8 tokens are small and stay in
+// L2): for MFMA step s (64 k) lane (j, kq) holds x[j][64s + 16kq .. +15].  The
+// contraction is order-free, so the A operand is built to match: those 16
+// positions are one 2-bit field of the 16 packed bytes of half kq%2 of block
+// s/2 (field 2*(s%2) + kq/2).  A lane loads its 16-byte half-block once per
+// block (lanes kq and kq^2 load the same bytes in the same instruction, which
+// the memory pipeline merges) and extracts the two fields it needs with one
+// shift and one mask per dword.  Each wave double-buffers its blocks: the
+// next block's A and B loads are in flight while the current one is used.
+#include "common.h"
+
+namespace bitnet {
+
+template <int MI, int NJ, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(
+    const uint8_t *__restrict__ packed, float alpha, int M, int K,
+    const int8_t *__restrict__ xq, const float *__restrict__ xs,
+    const int32_t *__restrict__ xsum, int N, int32_t *__restrict__ dot,
+    float *__restrict__ y) {
+    constexpr int BM = 16 * MI, BN = 16 * NJ;
+    constexpr int LDA = BN + 4;   // padded LDS row (ints): conflict-free ds_add
+    constexpr int NT = WAVES * 64;
+    __shared__ int acc_lds[BM * LDA];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int li = lane & 15, kq = lane >> 4;
+    const int m0 = blockIdx.x * BM;
+    for (int i = tid; i < BM * LDA; i += NT) acc_lds[i] = 0;
+
+    const int nblk = K >> 7;
+    const int b0 = (int)((int64_t)nblk * wv / WAVES);
+    const int b1 = (int)((int64_t)nblk * (wv + 1) / WAVES);
+    const int64_t rowb = K >> 2;
+
+    const uint8_t *prow[MI];
+    bool rok[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int m = m0 + mi * 16 + li;
+        rok[mi] = m < M;
+        prow[mi] = packed + (int64_t)(rok[mi] ? m : 0) * rowb + (kq & 1) * 16;
+    }
+    const int8_t *xrow[NJ];
+    bool tok[NJ];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int n = nj * 16 + li;
+        tok[nj] = n < N;
+        xrow[nj] = xq + (int64_t)(tok[nj] ? n : 0) * K + kq * 16;
+    }
+
+    v4i acc[MI][NJ];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = v4i{0, 0, 0, 0};
+
+    const v4i z = v4i{0, 0, 0, 0};
+    auto load = [&](int b, v4i *A, v4i (*B)[NJ]) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            A[mi] = rok[mi] ? __builtin_nontemporal_load(
+                                  reinterpret_cast<const v4i *>(prow[mi] + (int64_t)b * 32))
+                            : z;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj)
+                B[s2][nj] = tok[nj] ? *reinterpret_cast<const v4i *>(xrow[nj] + (int64_t)b * 128 + s2 * 64)
+                                    : z;
+    };
+    auto compute = [&](const v4i *A, v4i (*B)[NJ]) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int sh = 6 - 2 * (2 * s2 + (kq >> 1));
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const v4i a = v4i{(A[mi].x >> sh) & 0x03030303, (A[mi].y >> sh) & 0x03030303,
+                                  (A[mi].z >> sh) & 0x03030303, (A[mi].w >> sh) & 0x03030303};
+#pragma unroll
+                for (int nj = 0; nj < NJ; ++nj)
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, B[s2][nj], acc[mi][nj],
+                                                                        0, 0, 0);
+            }
+        }
+    };
+
+    v4i A0[MI], A1[MI];
+    v4i B0[2][NJ], B1[2][NJ];
+    if (b0 < b1) load(b0, A0, B0);
+    for (int b = b0; b < b1; b += 2) {
+        if (b + 1 < b1) load(b + 1, A1, B1);
+        compute(A0, B0);
+        if (b + 1 >= b1) break;
+        if (b + 2 < b1) load(b + 2, A0, B0);
+        compute(A1, B1);
+    }
+
+    __syncthreads();   // acc_lds zeroed by every thread before any add
+    // 16x16 result layout: lane l, register r holds row 4*(l/16)+r, column l%16
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                atomicAdd(&acc_lds[(mi * 16 + 4 * kq + r) * LDA + nj * 16 + li], acc[mi][nj][r]);
+    __syncthreads();
+    for (int i = tid; i < BM * BN; i += NT) {
+        const int n = i / BM, ml = i - n * BM;
+        const int m = m0 + ml;
+        if (n < N && m < M) {
+            const int d = acc_lds[ml * LDA + n] - xsum[n];
+            if (dot) dot[(int64_t)n * M + m] = d;
+            if (y) y[(int64_t)n * M + m] = ((float)d * alpha) / xs[n];
+        }
+    }
+}
+
+template <int MI, int NJ, int WAVES>
+static hipError_t run(const uint8_t *packed, float alpha, int64_t M, int64_t K, const int8_t *xq,
+                      const float *xs, const int32_t *xsum, int64_t N, int32_t *dot, float *y,
+                      hipStream_t st) {
+    const unsigned grid = (unsigned)((M + 16 * MI - 1) / (16 * MI));
+    hipLaunchKernelGGL((gemv_mfma_kernel<MI, NJ, WAVES>), dim3(grid), dim3(WAVES * 64), 0, st,
+                       packed, alpha, (int)M, (int)K, xq, xs, xsum, (int)N, dot, y);
+    return hipGetLastError();
+}
+
+template <int MI, int NJ>
+static hipError_t run_w(int waves, const uint8_t *packed, float alpha, int64_t M, int64_t K,
+                        const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                        int32_t *dot, float *y, hipStream_t st) {
+    // 16 waves (1024 threads) cap a wave at 128 VGPRs: only for small tiles
+    if constexpr (MI * NJ <= 2)
+        if (waves >= 16) return run<MI, NJ, 16>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    if (waves >= 8) return run<MI, NJ, 8>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    return run<MI, NJ, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+}
+
+template <int NJ>
+static hipError_t run_nj(const uint8_t *packed, float alpha, int64_t M, int64_t K,
+                         const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                         int32_t *dot, float *y, hipStream_t st) {
+    // waves split K: about two or more 128-weight blocks per wave
+    const int64_t nblk = K / 128;
+    const int waves = nblk >= 32 ? 16 : (nblk >= 16 ? 8 : 4);
+    // rows per workgroup: small matrices keep 16 rows per group (most groups in
+    // flight at once); large ones take 32 so each token tile is reused twice
+    if constexpr (NJ <= 2)
+        if (M >= 8192) return run_w<2, NJ>(waves, packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    return run_w<1, NJ>(waves, packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+}
+
+hipError_t launch_gemv_mfma(const uint8_t *packed, float alpha, int64_t M, int64_t K,
+                            const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                            int32_t *dot, float *y, hipStream_t st) {
+    if (N <= 16) return run_nj<1>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    if (N <= 32) return run_nj<2>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    if (N <= 48) return run_nj<3>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    return run_nj<4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+}
+
+}  // namespace bitnet
