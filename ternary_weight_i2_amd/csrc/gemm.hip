@@ -1,138 +1,235 @@
-// gemm.hip -- multi-token matmul on int8 MFMA (v_mfma_i32_16x16x64_i8).
+// gemm.hip -- multi-token (prefill) matmul on int8 MFMA (v_mfma_i32_32x32x32_i8).
 //
-// Pages: [P1] "BitNet 딥다이브" §4-2 (I2_S block interleave), §4-5 (separate
-// prefill path); [P2] "[분석/검증-3]" §3 and [P3] "[기술 분석 보고서]"
-// §3.2 (raw codes multiply the activations; the exact result subtracts
-// sum(x)).
+// Pages: [P1] "BitNet 딥다이브" §4-2 (I2_S block interleave), §4-5 (a separate
+// prefill path); [P2] "[분석/검증-3]" §3 and [P3] "[기술 분석 보고서]" §3.2 (raw
+// codes multiply the activations; the exact result subtracts sum(x)).
 //
-// The contraction over k is order-free, so the MFMA k-slots are assigned to
-// match the I2_S byte layout instead of shuffling the weights:
-//   one 16x16x64 step covers one half-block h (16 packed bytes per row);
-//   lane group kq (lanes 16kq..16kq+15) takes packed dword kq of that half,
-//   i.e. block bytes 16h+4kq..16h+4kq+3, whose four 2-bit fields i hold the
-//   positions 32i + 16h + 4kq + e (e = 0..3).
-// The A operand (weights, 16 bytes per lane) is that dword unpacked in
-// registers: byte 4i+e = field i of byte e = code of position 32i+16h+4kq+e.
-// The B operand (activations) must hold the same positions in the same byte
-// order; the activation tile is therefore staged in LDS with its 32 dwords per
-// block permuted so that those four dwords are contiguous and one 16-byte LDS
-// read fetches a lane's B operand.  MFMA accumulates the raw-code sum R in
-// int32; the epilogue writes D = R - sum(x) and y = D * alpha / s.
+// Tiling: a workgroup of WM x WN waves computes a BM x BN tile of the output
+// (weight rows x tokens); wave (wm, wn) owns a (32*MI) x (32*NJ) sub-tile made
+// of 32x32 MFMA tiles.  K advances one 128-weight I2_S block at a time.
+// Tiles are sized so every wave issues whole 1 KB DMA instructions per block.
+//
+// Operand layout.  For MFMA step s of a block (32 k each, s = 0..3) lane
+// (r, kg) -- r = lane%32, kg = lane/32 -- supplies 16 bytes for k = 32s + 16kg
+// + 0..15 of row/token r.  The B operand (tokens) is therefore a plain
+// 16-byte copy of the token row, and the tokens are staged in LDS in their
+// natural order (with an XOR swizzle of the 16-byte pieces inside a row so a
+// wave's reads spread over the banks).  The contraction is order-free, so the A operand is built to match:
+// those 16 positions are the 2-bit field s of the 16 packed bytes of half kg
+// of the row's block.  One 16-byte weight load per lane per block serves all
+// four steps (shift by 6-2s and mask per dword, no shuffle).  Weights are read
+// straight from global memory (they are small and shared through L2); tokens
+// go through LDS because all waves of a column share them.
+//
+// Pipelining: weight and token tiles move global -> LDS with the gfx950
+// LDS-DMA loads (global_load_lds_dwordx4: each lane's 16 bytes land at
+// M0 + 16*lane), three block stages deep, so no registers carry staged data
+// and the MFMAs of block kb overlap the loads of blocks kb+1 and kb+2; one
+// barrier per block.  Accumulators hold the raw-code sum R; the epilogue
+// writes D = R - sum(x) and y = D * alpha / s.
 #include "common.h"
 
 namespace bitnet {
 
-constexpr int kPkStride = 48;    // LDS bytes per packed-tile row (32 + pad)
-constexpr int kXStride = 144;    // LDS bytes per activation-tile row (128 + pad)
+#ifndef BITNET_GEMM_XCD_REMAP
+#define BITNET_GEMM_XCD_REMAP 1   // group each XCD's workgroups on shared token tiles
+#endif
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 
-// new dword slot of original block dword dd = 8i + 4h + kq
-__device__ __forceinline__ int xperm(int dd) {
-    const int i = dd >> 3, h = (dd >> 2) & 1, kq = dd & 3;
-    return (h * 4 + kq) * 4 + i;
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// s_waitcnt immediate that waits until at most `v` vector-memory operations of
+// this wave are outstanding and ignores the other counters (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int v>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(v >= 0 && v < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((v & 0xF) | (0x7 << 4) | (0xF << 8) | ((v >> 4) << 14));
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+// One LDS-DMA load: 16 bytes per lane from `g` to LDS address M0 + 16*lane.
+// Issued through inline asm so the compiler does not attach its conservative
+// "wait for every outstanding load" to later LDS reads; the kernel waits with
+// explicit vmcnt counts instead.  M0 is set here and used by nothing else in
+// the kernels that call this.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address (what M0 takes) of a pointer into a __shared__ array: the
+// low 32 bits of its generic address.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+template <int BM, int BN, int WM, int WN, int kStages>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
     const uint8_t *__restrict__ packed, float alpha, int M, int K,
     const int8_t *__restrict__ xq, const float *__restrict__ xs,
     const int32_t *__restrict__ xsum, int N, int32_t *__restrict__ dot,
     float *__restrict__ y) {
-    static_assert(WM * WN == 4, "four waves per workgroup");
-    constexpr int MI = BM / WM / 16;
-    constexpr int NJ = BN / WN / 16;
+    static_assert(kStages >= 2, "at least double buffering");
+    constexpr int NW = WM * WN;        // waves per workgroup
+    constexpr int MI = BM / WM / 32;   // 32-row MFMA tiles per wave
+    constexpr int NJ = BN / WN / 32;   // 32-token MFMA tiles per wave
     static_assert(MI >= 1 && NJ >= 1, "tile too small");
-    __shared__ __attribute__((aligned(16))) uint8_t pk[BM * kPkStride];
-    __shared__ __attribute__((aligned(16))) int8_t xt[BN * kXStride];
+    // LDS-DMA instructions per wave per block: each moves 64 lanes x 16 bytes.
+    constexpr int IA = BM / (32 * NW);  // weight tile: BM rows x 32 bytes
+    constexpr int IB = BN / (8 * NW);   // token tile: BN rows x 128 bytes
+    static_assert(IA >= 1 && IB >= 1 && BM % (32 * NW) == 0 && BN % (8 * NW) == 0,
+                  "tile shape: whole 1 KB DMA instructions per wave");
+    constexpr int A_BYTES = BM * kBlockBytes, B_BYTES = BN * kBlock;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
-    const int li = lane & 15, kq = lane >> 4;
-    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-    const int64_t prow_bytes = K >> 2;
-
-    v4i acc[MI][NJ];
-#pragma unroll
-    for (int a = 0; a < MI; ++a)
-#pragma unroll
-        for (int b = 0; b < NJ; ++b) acc[a][b] = v4i{0, 0, 0, 0};
-
+    const int r32 = lane & 31, kg = lane >> 5;
+    // Tile of this workgroup.  Workgroups are dealt to the XCDs round-robin
+    // (id % 8); renumbering so that each XCD gets a contiguous run of tiles,
+    // M-tile fastest, makes the workgroups of one XCD share token tiles in its
+    // L2 instead of every XCD fetching every token tile.
+    const int mtiles = (M + BM - 1) / BM;
+    const int total = (int)gridDim.x;
+    int id = (int)blockIdx.x;
+#if BITNET_GEMM_XCD_REMAP
+    if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+#endif
+    const int m0 = (id % mtiles) * BM, n0 = (id / mtiles) * BN;
+    const int64_t rowb = K >> 2;
     const int nkb = K / kBlock;
+
+    // Global source of this lane's 16 bytes in each DMA instruction.  Rows and
+    // tokens past the matrix are clamped to the last valid one (their results
+    // are never stored).  Token rows are XOR-swizzled: LDS slot c' of row r
+    // holds piece c' ^ (r & 7), which spreads a wave's B reads over the banks.
+    const uint8_t *asrc[IA];
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+        const int row = 32 * (wave * IA + i) + (lane >> 1);
+        asrc[i] = packed + (int64_t)min(m0 + row, M - 1) * rowb + 16 * (lane & 1);
+    }
+    const int8_t *bsrc[IB];
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        const int row = 8 * (wave * IB + i) + (lane >> 3);
+        const int piece = (lane & 7) ^ (row & 7);
+        bsrc[i] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
+    }
+    auto issue = [&](int kb, int st) {
+        const int8_t *base = lds + st * STAGE;
+#pragma unroll
+        for (int i = 0; i < IA; ++i)
+            dma16(asrc[i] + (int64_t)kb * kBlockBytes, lds_addr_of(base + 1024 * (wave * IA + i)));
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+            dma16(bsrc[i] + (int64_t)kb * kBlock,
+                  lds_addr_of(base + A_BYTES + 1024 * (wave * IB + i)));
+    };
+
+    v16i acc[MI][NJ];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][nj][e] = 0;
+
+    // Always kStages-1 blocks in flight (past the end the last block is
+    // re-fetched into a stage that is never read), so the wait below is a
+    // constant: at most (kStages-2) newer blocks of DMA may still be pending.
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p) issue(min(p, nkb - 1), p);
     for (int kb = 0; kb < nkb; ++kb) {
-        for (int c = tid; c < BM * 2; c += 256) {
-            const int r = c >> 1, h = c & 1;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (m0 + r < M)
-                v = *reinterpret_cast<const int4 *>(packed + (int64_t)(m0 + r) * prow_bytes +
-                                                    kb * kBlockBytes + h * 16);
-            *reinterpret_cast<int4 *>(pk + r * kPkStride + h * 16) = v;
-        }
-        for (int c = tid; c < BN * 8; c += 256) {
-            const int r = c >> 3, q = c & 7;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (n0 + r < N)
-                v = *reinterpret_cast<const int4 *>(xq + (int64_t)(n0 + r) * K +
-                                                    kb * kBlock + q * 16);
-            int *dst = reinterpret_cast<int *>(xt + r * kXStride);
-            dst[xperm(4 * q + 0)] = v.x;
-            dst[xperm(4 * q + 1)] = v.y;
-            dst[xperm(4 * q + 2)] = v.z;
-            dst[xperm(4 * q + 3)] = v.w;
-        }
-        __syncthreads();
+        wait_vmcnt<(IA + IB) * (kStages - 2)>();
+        __syncthreads();   // every wave's share of block kb is in LDS; stage (kb-1) is free
+        issue(min(kb + kStages - 1, nkb - 1), (kb + kStages - 1) % kStages);
+        const int8_t *sa = lds + (kb % kStages) * STAGE;
+        const int8_t *sb = sa + A_BYTES;
+        v4i a[MI];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v4i a[MI], b[NJ];
+        for (int mi = 0; mi < MI; ++mi)
+            a[mi] = *reinterpret_cast<const v4i *>(sa + ((wm * MI + mi) * 32 + r32) * kBlockBytes +
+                                                   16 * kg);
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const uint32_t p = *reinterpret_cast<const uint32_t *>(
-                    pk + ((wm * MI + mi) * 16 + li) * kPkStride + h * 16 + kq * 4);
-                a[mi] = v4i{(int)((p >> 6) & 0x03030303u), (int)((p >> 4) & 0x03030303u),
-                            (int)((p >> 2) & 0x03030303u), (int)(p & 0x03030303u)};
+        for (int s = 0; s < 4; ++s) {
+            const int sh = 6 - 2 * s;
+            v4i af[MI], bf[NJ];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                af[mi] = v4i{(a[mi].x >> sh) & 0x03030303, (a[mi].y >> sh) & 0x03030303,
+                             (a[mi].z >> sh) & 0x03030303, (a[mi].w >> sh) & 0x03030303};
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj) {
+                const int row = (wn * NJ + nj) * 32 + r32;
+                bf[nj] = *reinterpret_cast<const v4i *>(
+                    sb + row * kBlock + 16 * ((2 * s + kg) ^ (row & 7)));
             }
-#pragma unroll
-            for (int nj = 0; nj < NJ; ++nj)
-                b[nj] = *reinterpret_cast<const v4i *>(
-                    xt + ((wn * NJ + nj) * 16 + li) * kXStride + (h * 4 + kq) * 16);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int nj = 0; nj < NJ; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mi], b[nj],
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[nj],
                                                                         acc[mi][nj], 0, 0, 0);
         }
-        __syncthreads();
     }
+    wait_vmcnt<0>();   // drain the trailing re-fetches before the workgroup ends
 
-    // 16x16 result layout: lane l, register r holds row 4*(l/16)+r, column l%16
+    // 32x32 result layout: lane l, register 4q + j holds row 8q + 4*(l/32) + j,
+    // column l%32; four consecutive rows per q go out as one 16-byte store
+    // where the output rows allow it.
+    const bool vec_ok = (M & 3) == 0 && ((reinterpret_cast<uintptr_t>(dot) |
+                                          reinterpret_cast<uintptr_t>(y)) & 15) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int n = n0 + (wn * NJ + nj) * 32 + r32;
+        if (n >= N) continue;
+        const int sx = xsum[n];
+        const float s = xs[n];
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            const int n = n0 + (wn * NJ + nj) * 16 + li;
-            if (n >= N) continue;
-            const int sx = xsum[n];
-            const float s = xs[n];
+        for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + (wm * MI + mi) * 16 + 4 * kq + r;
-                if (m < M) {
-                    const int d = acc[mi][nj][r] - sx;
-                    if (dot) dot[(int64_t)n * M + m] = d;
-                    if (y) y[(int64_t)n * M + m] = ((float)d * alpha) / s;
+            for (int q = 0; q < 4; ++q) {
+                const int mb = m0 + (wm * MI + mi) * 32 + 8 * q + 4 * kg;
+                int d[4];
+                float yv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    d[j] = acc[mi][nj][4 * q + j] - sx;
+                    yv[j] = ((float)d[j] * alpha) / s;
+                }
+                const int64_t o = (int64_t)n * M + mb;
+                if (vec_ok && mb + 3 < M) {
+                    if (dot) *reinterpret_cast<int4 *>(dot + o) = make_int4(d[0], d[1], d[2], d[3]);
+                    if (y) *reinterpret_cast<float4 *>(y + o) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (mb + j < M) {
+                            if (dot) dot[o + j] = d[j];
+                            if (y) y[o + j] = yv[j];
+                        }
+                    }
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 static hipError_t run_gemm(const uint8_t *packed, float alpha, int64_t M, int64_t K,
                            const int8_t *xq, const float *xs, const int32_t *xsum,
                            int64_t N, int32_t *dot, float *y, hipStream_t st) {
-    const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN>), grid, dim3(256), 0, st, packed,
-                       alpha, (int)M, (int)K, xq, xs, xsum, (int)N, dot, y);
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, S>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0,
+                       st, packed, alpha, (int)M, (int)K, xq, xs, xsum, (int)N, dot, y);
     return hipGetLastError();
 }
 
@@ -140,11 +237,10 @@ hipError_t launch_gemm_mfma(const uint8_t *packed, float alpha, int64_t M,
                             int64_t K, const int8_t *xq, const float *xs,
                             const int32_t *xsum, int64_t N, int32_t *dot,
                             float *y, hipStream_t st) {
-    if (N <= 16) return run_gemm<64, 16, 4, 1>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
-    if (N <= 32) return run_gemm<64, 32, 4, 1>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
-    if (N <= 64 || M * N < 256LL * 128 * 128)
-        return run_gemm<64, 64, 2, 2>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
-    return run_gemm<128, 128, 2, 2>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    // token tile matched to small N so no MFMA column work is wasted
+    if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    return run_gemm<128, 128, 2, 2, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
 }
 
 }  // namespace bitnet

@@ -274,13 +274,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
     const int ngroups = (row1 - row0 + RG * kGemvWaves - 1) / (RG * kGemvWaves);
     auto group_row = [&](int g) { return row0 + (g * kGemvWaves + wv) * RG + sub; };
 #endif
-    const int4 zero4 = make_int4(0, 0, 0, 0);
-
     // Every lane issues exactly JM loads per row group, from a clamped (always
     // valid) address; lanes or rows outside the matrix are zeroed after the
     // load.  A fixed, branch-free load count lets the compiler wait for just
     // the row group in use while the next one is still in flight.
-    int4 cur[JM], nxt[JM];
+    int4 cur[JM];
+#if BITNET_GEMV_PIPE
+    int4 nxt[JM];
+#endif
     auto load_group = [&](int g, int4 *r) {
         const int row = min(group_row(g), M - 1);
         const v4i *prow = reinterpret_cast<const v4i *>(packed + (int64_t)row * (K >> 2));
