@@ -28,6 +28,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+# HBM bytes per launch of the fused GEMV, from rocprofv3 FETCH_SIZE (x2.0) and
+# WRITE_SIZE (x1.0) scaled by a 256 MiB copy (profiles/gemv_b2_decode_hbm_traffic.md);
+# valid only for the kernel sources with this sha256.
+TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv.hip", "ternary_weight_i2_amd/csrc/common.h"),
+           "sha256": "1bcd9a555bdeff19c87aa1bccb30f33f23253c48b597d7e714ebb66f1cb986aa",
+           "bytes_per_launch": 4589056}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
@@ -43,7 +49,36 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the secondary per-row measurements")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy three times "
+                         "(calibrates HBM byte counters) and exit")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 256 << 20
+
+
+def measured_traffic():
+    """The recorded per-launch HBM bytes, or None once the kernel changed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC["bytes_per_launch"] if h.hexdigest() == TRAFFIC["sha256"] else None
+
+
+def copy_probe():
+    """A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+    calibrates the counters taken on the library kernels."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "repeats": 3}), flush=True)
 
 
 def build_stack(bn, synth, torch, layers):
@@ -301,6 +336,10 @@ def main():
               "the sharded layout is described in DESIGN.md but not built.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_probe:
+        torch.cuda.set_device(0)
+        copy_probe()
+        return
 
     import ternary_weight_i2_amd as bn
     from ternary_weight_i2_amd import synth
@@ -361,7 +400,7 @@ def main():
                    "unfused_graph_ms_per_step": round(unfused_ms, 4)},
         "roofline": {"bound": "hbm", "kernel": "gemv_valu_kernel<1,PF,2> (fused bf16 quantise + GEMV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(per_launch_s * 1e6, 3)},
         "cpu_baseline": cpu,
         "rows": rows,
