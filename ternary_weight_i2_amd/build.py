@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libbitnet_i2s.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,10 +28,7 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *sources(), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,9 +36,25 @@ def build(verbose: bool = False) -> str:
             if "packed-fp32-ops" not in ln and ln.strip()]
     if res.returncode != 0:
         sys.stderr.write("\n".join(errs) + "\n")
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd[-3:])}")
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile each translation unit in parallel, then link the shared library."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    srcs = sources()
+    with tempfile.TemporaryDirectory(prefix="bitnet_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+        jobs = [[HIPCC, *FLAGS, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), jobs))
+        tmp = OUT + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, OUT)
     return OUT
 

@@ -182,10 +182,9 @@ BITNET_API int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
     return ok();
 }
 
-BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
-                                 const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq,
-                                 float *x_scale, int32_t *x_sum, void *stream) {
-    const char *fn = "bitnet_linear_i2s";
+static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int64_t K,
+                       const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq, float *x_scale,
+                       int32_t *x_sum, void *stream) {
     if (dtype != BITNET_F32 && dtype != BITNET_BF16)
         return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
     if (N < 0 || N > BITNET_GEMV_MAX_N)
@@ -231,6 +230,13 @@ BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
                 e = bitnet::launch_gemv_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
                                              x_sum, N, gm[i].dot, gm[i].y, st);
     }
-    if (e != hipSuccess) return hip_fail("bitnet_linear_i2s: launch", e);
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
+}
+
+BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
+                                 const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq,
+                                 float *x_scale, int32_t *x_sum, void *stream) {
+    return linear_impl("bitnet_linear_i2s", x, dtype, N, K, mats, n_mats, xq, x_scale, x_sum,
+                       stream);
 }

@@ -11,6 +11,7 @@ namespace bitnet {
 // of block positions j, j+32, j+64, j+96 in bits 7-6, 5-4, 3-2, 1-0.
 constexpr int kBlock = 128;
 constexpr int kBlockBytes = 32;
+constexpr int kXcds = 8;   // MI355X: 8 XCDs (own L2 each); workgroups dealt round-robin
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -19,16 +20,78 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// Wave-wide (64 lanes) sums and maxima through cross-lane shuffles.
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane moves inside a row of 16 lanes through DPP (no LDS round trip).
+// Controls: quad_perm [1,0,3,2] and [2,3,0,1] swap neighbours at distance 1
+// and 2; row_half_mirror reads lane 7-i of each 8-lane half row; row_mirror
+// reads lane 15-i of the row.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+
+// Sum over each aligned group of L lanes (L = 8, 16, 32 or 64); every lane of
+// the group receives the sum.  Once neighbours at distance 1 and 2 are added
+// every lane holds its quad's sum, so mirroring within 8 and then 16 lanes
+// pairs whole quads and then whole halves; the two cross-row steps shuffle.
+template <int L>
+__device__ __forceinline__ int group_sum_i32(int v) {
+    static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group of 8..64 lanes");
+    v += dpp_i32<kDppXor1>(v);
+    v += dpp_i32<kDppXor2>(v);
+    v += dpp_i32<kDppHalfMirror>(v);
+    if constexpr (L >= 16) v += dpp_i32<kDppMirror>(v);
+    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
     return v;
 }
+__device__ __forceinline__ int wave_sum_i32(int v) { return group_sum_i32<64>(v); }
+// Wave-wide maximum (fmaxf ignores a NaN operand, so the order is immaterial).
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
     return v;
+}
+
+// s_waitcnt immediate that waits until at most `v` vector-memory operations of
+// this wave are outstanding and ignores the other counters (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int v>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(v >= 0 && v < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((v & 0xF) | (0x7 << 4) | (0xF << 8) | ((v >> 4) << 14));
+}
+
+// One LDS-DMA load: 16 bytes per lane from `g` to LDS address M0 + 16*lane.
+// Issued through inline asm so the compiler does not attach its conservative
+// "wait for every outstanding load" to later LDS reads; the kernel waits with
+// explicit vmcnt counts instead.  M0 is set here and used by nothing else in
+// the kernels that call this.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address (what M0 takes) of a pointer into a __shared__ array: the
+// low 32 bits of its generic address.
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 // Per-token quantisation arithmetic, shared by the stand-alone quantiser and

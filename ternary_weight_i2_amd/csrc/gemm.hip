@@ -34,39 +34,8 @@ namespace bitnet {
 #ifndef BITNET_GEMM_XCD_REMAP
 #define BITNET_GEMM_XCD_REMAP 1   // group each XCD's workgroups on shared token tiles
 #endif
-constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-// s_waitcnt immediate that waits until at most `v` vector-memory operations of
-// this wave are outstanding and ignores the other counters (gfx9 encoding:
-// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
-template <int v>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(v >= 0 && v < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((v & 0xF) | (0x7 << 4) | (0xF << 8) | ((v >> 4) << 14));
-}
-
-// One LDS-DMA load: 16 bytes per lane from `g` to LDS address M0 + 16*lane.
-// Issued through inline asm so the compiler does not attach its conservative
-// "wait for every outstanding load" to later LDS reads; the kernel waits with
-// explicit vmcnt counts instead.  M0 is set here and used by nothing else in
-// the kernels that call this.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(lds_addr)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// LDS byte address (what M0 takes) of a pointer into a __shared__ array: the
-// low 32 bits of its generic address.
-__device__ __forceinline__ uint32_t lds_addr_of(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
 
 template <int BM, int BN, int WM, int WN, int kStages>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(

@@ -1,0 +1,464 @@
+// gemv_valu.h -- decode matmul (a few tokens) on the vector ALUs: the kernel
+// template, instantiated per token count in gemv_valu_n{1,2,4,8}.hip (so the
+// four compile in parallel) and launched from gemv.hip.
+//
+// Pages: [P2] "[분석/검증-3] BitNet.cpp ARM 커널 재작성" §3 and [P3] "[기술 분석
+// 보고서] ARM64 ... 1.58-bit ..." §3.1-§4 (raw codes 0/1/2 multiply the
+// activations at offsets k, k+32, k+64, k+96 of a block; the scale is applied
+// by the caller); [P1] "BitNet 딥다이브" §2-1 (decode is bound by reading the
+// weights), §4-3 (a weight block is loaded once and reused for several
+// activation columns), §4-5 (per-token activation scale).
+//
+// Work split (gfx950, wave64): a workgroup of 4 waves owns `rows_per_wg`
+// consecutive rows of one matrix, walked in row groups (see the kernel).  A
+// row is read as 16-byte chunks (coalesced dwordx4 loads, each packed byte
+// fetched exactly once).  A 16-byte chunk c is
+// half an I2_S block (b = c/2, half h = c%2): dword j holds block bytes
+// 16h+4j..16h+4j+3 and so the codes of positions 32i + 16h + 4j + e.
+// Masking a dword keeps one 2-bit field per byte and v_dot4_i32_i8 multiplies
+// it with four contiguous int8 activations:
+//   field i=3 (bits 1-0): w & 0x03030303        -> code * 1
+//   field i=2 (bits 3-2): w & 0x0C0C0C0C        -> code * 4
+//   field i=1 (bits 5-4): w & 0x30303030        -> code * 16
+//   field i=0 (bits 7-6): (w >> 2) & 0x30303030 -> code * 16
+// Three accumulators (x1, x4, x16) avoid per-field shifts; acc1 + acc4/4 +
+// acc16/16 is the raw-code sum R exactly, and D = R - sum(x).
+//
+// Activations live in LDS in a group-major layout: token t, field i, chunk c
+// at byte t*K + i*(K/4) + 16c holds x[128*(c/2) + 32i + 16*(c%2) + 0..15],
+// so the four 16-byte reads a lane makes per chunk are contiguous across the
+// wave (no bank conflicts).  Before the activations are staged, each wave has
+// already issued the loads of its first row group, so the two memory
+// latencies overlap.  A workgroup usually owns a single row group; where it
+// owns several, each group is loaded and then consumed (a ping-pong register
+// prefetch, BITNET_GEMV_PIPE=1, measured slower on gfx950).
+//
+// Modes: 0 = int8 xq (+ scale and sum) from global memory; 1/2 = fp32/bf16
+// tokens quantised in the prologue with the same arithmetic as the
+// stand-alone quantiser (every workgroup recomputes the identical values;
+// workgroup 0 optionally stores them).  One launch may serve up to kMaxMats
+// matrices that share the tokens (e.g. q/k/v, or gate/up).
+#pragma once
+#include "common.h"
+
+namespace bitnet {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kLdsBytes = 61440;   // activation staging budget per workgroup (60 KiB)
+#ifndef BITNET_GEMV_TARGET_WGS
+#define BITNET_GEMV_TARGET_WGS 1024   // workgroups per launch before slabs grow
+#endif
+#ifndef BITNET_GEMV_LPR
+#define BITNET_GEMV_LPR 0             // 0: pick lanes per row from K
+#endif
+#ifndef BITNET_GEMV_PIPE
+#define BITNET_GEMV_PIPE 0            // 1: ping-pong register prefetch of the next row group
+#endif
+#ifndef BITNET_GEMV_INTERLEAVE
+#define BITNET_GEMV_INTERLEAVE 0      // 1: workgroups take row groups round-robin
+#endif
+
+template <int MODE>
+struct TokVec;   // 16 bytes of a token row, widened to fp32
+template <>
+struct TokVec<1> {
+    static constexpr int kElems = 4;
+    __device__ static void widen(const uint4 u, float *v) {
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    }
+    __device__ static void load(const char *row, int q, float *v) {
+        widen(reinterpret_cast<const uint4 *>(row)[q], v);
+    }
+};
+template <>
+struct TokVec<2> {
+    static constexpr int kElems = 8;
+    __device__ static void widen(const uint4 u, float *v) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = __uint_as_float(w[j] << 16);            // low half = lower element
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+    }
+    __device__ static void load(const char *row, int q, float *v) {
+        widen(reinterpret_cast<const uint4 *>(row)[q], v);
+    }
+};
+
+// LDS byte offset of activation element k of token t (group-major layout)
+__device__ __forceinline__ int lds_pos(int t, int K, int k) {
+    const int b = k >> 7, i = (k >> 5) & 3, h = (k >> 4) & 1, e = k & 15;
+    return t * K + i * (K >> 2) + 32 * b + 16 * h + e;
+}
+
+// Quantise ntok tokens of x (fp32 or bf16) into LDS; per-token s and sum
+// land in s_tok / sum_tok.  Workgroup 0 also writes the optional outputs.
+// Short tokens (at most XR 16-byte pieces per thread) take the register path:
+// load_tokens() issues every piece load up front -- before the caller issues
+// its weight loads, so waiting for the tokens never waits for the weights --
+// from clamped, always-valid addresses (a repeated last piece cannot change
+// the absmax and is not emitted); finish() then reduces and quantises.
+// Longer tokens are streamed through twice (absmax pass, quantise pass).
+template <int NT, int MODE>
+struct TokenPrologue {
+    using V = TokVec<MODE>;
+    static constexpr int E = V::kElems;
+    static constexpr int XR = NT == 1 ? 4 : (NT == 2 ? 2 : 1);   // register budget
+    uint4 raw[NT][XR];      // token bits as loaded; widened only in finish()
+
+    __device__ static bool fits(const GemvArgs &a) {
+        return NT <= 2 && a.K / E <= XR * kGemvThreads;
+    }
+    __device__ void load_tokens(const GemvArgs &a) {
+        const int nq = a.K / E;
+        const char *x = reinterpret_cast<const char *>(a.x);
+        const int rowb = a.K * (MODE == 2 ? 2 : 4);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int tt = min(t, a.ntok - 1);
+#pragma unroll
+            for (int r = 0; r < XR; ++r)
+                raw[t][r] = reinterpret_cast<const uint4 *>(x + tt * rowb)[min(
+                    (int)threadIdx.x + r * kGemvThreads, nq - 1)];
+        }
+    }
+    __device__ void finish(const GemvArgs &a, bool in_regs, int8_t *xl, float *s_tok,
+                           int *sum_tok, float (*redf)[NT], int (*redi)[NT]) {
+        const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+        const int K = a.K, nq = K / E;
+        const char *x = reinterpret_cast<const char *>(a.x);
+        const int rowb = K * (MODE == 2 ? 2 : 4);
+        float am[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            am[t] = 0.0f;
+            if (t < a.ntok) {
+                if (in_regs) {
+#pragma unroll
+                    for (int r = 0; r < XR; ++r) {
+                        float v[E];
+                        V::widen(raw[t][r], v);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) am[t] = fmaxf(am[t], fabsf(v[e]));
+                    }
+                } else {
+                    for (int q = tid; q < nq; q += kGemvThreads) {
+                        float v[E];
+                        V::load(x + t * rowb, q, v);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) am[t] = fmaxf(am[t], fabsf(v[e]));
+                    }
+                }
+            }
+            am[t] = wave_max_f32(am[t]);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) redf[wv][t] = am[t];
+        }
+        __syncthreads();
+        float s[NT];
+        int sm[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            s[t] = quant_scale(fmaxf(fmaxf(redf[0][t], redf[1][t]), fmaxf(redf[2][t], redf[3][t])));
+            sm[t] = 0;
+        }
+        const bool store = blockIdx.x == 0 && a.xq_out != nullptr;
+        auto emit = [&](int t, int q, const float *v) {
+            uint32_t pq[E / 4];
+#pragma unroll
+            for (int j = 0; j < E / 4; ++j) pq[j] = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int qi = quant_one(v[e], s[t]);
+                sm[t] += qi;
+                pq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+            }
+            const int pos = lds_pos(t, K, q * E);
+            if constexpr (E == 8) {
+                const uint2 u = make_uint2(pq[0], pq[E / 4 - 1]);
+                *reinterpret_cast<uint2 *>(xl + pos) = u;
+                if (store) reinterpret_cast<uint2 *>(a.xq_out + (int64_t)t * K)[q] = u;
+            } else {
+                *reinterpret_cast<uint32_t *>(xl + pos) = pq[0];
+                if (store) reinterpret_cast<uint32_t *>(a.xq_out + (int64_t)t * K)[q] = pq[0];
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < a.ntok) {
+                if (in_regs) {
+#pragma unroll
+                    for (int r = 0; r < XR; ++r) {
+                        const int q = tid + r * kGemvThreads;
+                        float v[E];
+                        V::widen(raw[t][r], v);
+                        if (q < nq) emit(t, q, v);
+                    }
+                } else {
+                    for (int q = tid; q < nq; q += kGemvThreads) {
+                        float v[E];
+                        V::load(x + t * rowb, q, v);
+                        emit(t, q, v);
+                    }
+                }
+            }
+            sm[t] = wave_sum_i32(sm[t]);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) redi[wv][t] = sm[t];
+        }
+        __syncthreads();
+        if (tid < NT && tid < a.ntok) {
+            const int total = redi[0][tid] + redi[1][tid] + redi[2][tid] + redi[3][tid];
+            s_tok[tid] = s[tid];
+            sum_tok[tid] = total;
+            if (blockIdx.x == 0) {
+                if (a.xs_out) a.xs_out[tid] = s[tid];
+                if (a.xsum_out) a.xsum_out[tid] = total;
+            }
+        }
+    }
+};
+
+// Work split: a wave handles row groups of 64/LPR rows, LPR lanes per row;
+// lane u of a row takes the row's 16-byte chunks u, u+LPR, ..., at most JM of
+// them (J = ceil(C/LPR) at run time).  The host picks LPR per launch (see
+// pick_lpr): small launches spread a row over more lanes (2B-class q/k/v and o
+// at K=2560: 16 lanes x 3 chunks; down at K=6912: 32 x 4), large ones keep
+// J close to 8 (K=8192: 16 x 8; K=28672: 64 x 7).  All J loads of a row group
+// are in flight together.
+#ifndef BITNET_GEMV_XDIRECT
+#define BITNET_GEMV_XDIRECT 0         // 1: mode 0 reads int8 tokens from global memory
+#endif
+#ifndef BITNET_GEMV_JM
+#define BITNET_GEMV_JM 8              // chunks per lane per row group (upper bound)
+#endif
+
+template <int NT, int LPR, int MODE>
+__global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs a) {
+    constexpr int JM = BITNET_GEMV_JM;
+    constexpr int RG = 64 / LPR;            // rows per wave per row group
+    extern __shared__ int4 lds[];
+    int8_t *xl = reinterpret_cast<int8_t *>(lds);
+    __shared__ float s_tok[NT];
+    __shared__ int sum_tok[NT];
+    __shared__ float redf[kGemvWaves][NT];
+    __shared__ int redi[kGemvWaves][NT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int sub = lane / LPR, u = lane % LPR;
+    int mi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+        if (i < a.nmats && (int)blockIdx.x >= a.mat[i].wg_begin) mi = i;
+    const uint8_t *packed = a.mat[mi].packed;
+    const int M = a.mat[mi].M;
+    const int K = a.K;
+    const int C = K >> 6;                       // 16-byte chunks per packed row
+    const int J = (C + LPR - 1) / LPR;
+    const int wg_local = (int)blockIdx.x - a.mat[mi].wg_begin;
+#if BITNET_GEMV_INTERLEAVE
+    // row group g of this workgroup is global row group wg_local + g * nwg:
+    // at any moment the whole launch reads one compact band of the matrix
+    const int nwg = (mi + 1 < a.nmats ? a.mat[mi + 1].wg_begin : (int)gridDim.x) - a.mat[mi].wg_begin;
+    const int GR = RG * kGemvWaves;                 // rows per row group
+    const int ngroups_all = (M + GR - 1) / GR;
+    const int ngroups = wg_local < ngroups_all ? (ngroups_all - wg_local + nwg - 1) / nwg : 0;
+    const int row1 = M;
+    auto group_row = [&](int g) { return (wg_local + g * nwg) * GR + wv * RG + sub; };
+#else
+    const int row0 = wg_local * a.rows_per_wg;
+    const int row1 = min(M, row0 + a.rows_per_wg);
+    // row groups of this wave: rows row0 + (g*4 + wv)*RG + sub
+    const int ngroups = (row1 - row0 + RG * kGemvWaves - 1) / (RG * kGemvWaves);
+    auto group_row = [&](int g) { return row0 + (g * kGemvWaves + wv) * RG + sub; };
+#endif
+    // Every lane issues exactly JM loads per row group, from a clamped (always
+    // valid) address; lanes or rows outside the matrix are zeroed after the
+    // load.  A fixed, branch-free load count lets the compiler wait for just
+    // the row group in use while the next one is still in flight.
+    int4 cur[JM];
+#if BITNET_GEMV_PIPE
+    int4 nxt[JM];
+#endif
+    auto load_group = [&](int g, int4 *r) {
+        const int row = min(group_row(g), M - 1);
+        const v4i *prow = reinterpret_cast<const v4i *>(packed + (int64_t)row * (K >> 2));
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int c = min(u + LPR * j, C - 1);
+            const v4i v = __builtin_nontemporal_load(prow + c);
+            r[j] = make_int4(v.x, v.y, v.z, v.w);
+        }
+    };
+    // ---- activations -> LDS (group-major), per-token scale and sum ----
+    // Token loads are issued first, then the first row group's weight loads,
+    // so the token work below overlaps the weight latency.
+    constexpr bool kDirect = MODE == 0 && BITNET_GEMV_XDIRECT;
+    if constexpr (kDirect) {
+        load_group(0, cur);
+        if (tid < NT && tid < a.ntok) {
+            s_tok[tid] = a.xs_in[tid];
+            sum_tok[tid] = a.xsum_in[tid];
+        }
+    } else if constexpr (MODE == 0) {
+        const int n16 = a.ntok * (K >> 4);
+        const int4 *src = reinterpret_cast<const int4 *>(a.x);
+        if (n16 <= 2 * kGemvThreads) {           // two int4 pieces per thread in registers
+            const int q0 = tid, q1 = tid + kGemvThreads;
+            const int4 p0 = src[min(q0, n16 - 1)];
+            const int4 p1 = src[min(q1, n16 - 1)];
+            __builtin_amdgcn_sched_barrier(0);   // keep the token loads ahead of the weights
+            load_group(0, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kp = K >> 4;
+            if (q0 < n16) {
+                const int t = q0 / kp;
+                *reinterpret_cast<int4 *>(xl + lds_pos(t, K, (q0 - t * kp) << 4)) = p0;
+            }
+            if (q1 < n16) {
+                const int t = q1 / kp;
+                *reinterpret_cast<int4 *>(xl + lds_pos(t, K, (q1 - t * kp) << 4)) = p1;
+            }
+        } else {
+            load_group(0, cur);
+            for (int q = tid; q < n16; q += kGemvThreads) {
+                const int t = q / (K >> 4), k = (q - t * (K >> 4)) << 4;
+                *reinterpret_cast<int4 *>(xl + lds_pos(t, K, k)) = src[q];
+            }
+        }
+        if (tid < NT && tid < a.ntok) {
+            s_tok[tid] = a.xs_in[tid];
+            sum_tok[tid] = a.xsum_in[tid];
+        }
+    } else {
+        TokenPrologue<NT, MODE> tp;
+        const bool in_regs = TokenPrologue<NT, MODE>::fits(a);
+        if (in_regs) tp.load_tokens(a);
+        __builtin_amdgcn_sched_barrier(0);       // keep the token loads ahead of the weights
+        load_group(0, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        tp.finish(a, in_regs, xl, s_tok, sum_tok, redf, redi);
+    }
+    __syncthreads();
+
+    const int gstride = K >> 2;   // bytes between fields in LDS
+    int32_t *dot = a.mat[mi].dot;
+    float *y = a.mat[mi].y;
+    const float alpha = a.mat[mi].alpha;
+    auto compute = [&](int g, const int4 *w) {
+        const bool row_ok = group_row(g) < row1;
+        int a1[NT], a4[NT], a16[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) a1[t] = a4[t] = a16[t] = 0;
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int c = u + LPR * j;
+            if (j < J) {
+                const bool ok = c < C && row_ok;
+                const int pw[4] = {ok ? w[j].x : 0, ok ? w[j].y : 0, ok ? w[j].z : 0,
+                                   ok ? w[j].w : 0};
+                const int cl = min(c, C - 1);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    if (t < a.ntok) {
+                        int4 x0, x1, x2, x3;
+                        if constexpr (kDirect) {
+                            const int8_t *xg = reinterpret_cast<const int8_t *>(a.x) + t * K +
+                                               kBlock * (cl >> 1) + 16 * (cl & 1);
+                            x0 = *reinterpret_cast<const int4 *>(xg);
+                            x1 = *reinterpret_cast<const int4 *>(xg + 32);
+                            x2 = *reinterpret_cast<const int4 *>(xg + 64);
+                            x3 = *reinterpret_cast<const int4 *>(xg + 96);
+                        } else {
+                            const int8_t *xt = xl + t * K + 16 * cl;
+                            x0 = *reinterpret_cast<const int4 *>(xt);
+                            x1 = *reinterpret_cast<const int4 *>(xt + gstride);
+                            x2 = *reinterpret_cast<const int4 *>(xt + 2 * gstride);
+                            x3 = *reinterpret_cast<const int4 *>(xt + 3 * gstride);
+                        }
+                        const int xv0[4] = {x0.x, x0.y, x0.z, x0.w};
+                        const int xv1[4] = {x1.x, x1.y, x1.z, x1.w};
+                        const int xv2[4] = {x2.x, x2.y, x2.z, x2.w};
+                        const int xv3[4] = {x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            a16[t] = dot4((pw[d] >> 2) & 0x30303030, xv0[d], a16[t]);
+                            a16[t] = dot4(pw[d] & 0x30303030, xv1[d], a16[t]);
+                            a4[t] = dot4(pw[d] & 0x0C0C0C0C, xv2[d], a4[t]);
+                            a1[t] = dot4(pw[d] & 0x03030303, xv3[d], a1[t]);
+                        }
+                    }
+                }
+            }
+        }
+        const int row = group_row(g);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < a.ntok) {
+                // a4 and a16 are exact multiples of 4 and 16
+                const int r = group_sum_i32<LPR>(a1[t] + (a4[t] >> 2) + (a16[t] >> 4));
+                if (u == t && row_ok) {
+                    const int d = r - sum_tok[t];
+                    if (dot) dot[(int64_t)t * M + row] = d;
+                    if (y) y[(int64_t)t * M + row] = ((float)d * alpha) / s_tok[t];
+                }
+            }
+        }
+    };
+    // Default: load a row group, then consume it.  BITNET_GEMV_PIPE=1 keeps two
+    // register buffers in ping-pong (the next group's loads issued before the
+    // current group is used; past the last group the loads repeat the last
+    // group's cached addresses).
+#if !BITNET_GEMV_PIPE
+    for (int g = 0; g < ngroups; ++g) {
+        if (g > 0) load_group(g, cur);
+        compute(g, cur);
+    }
+#else
+    if (ngroups == 1) {
+        compute(0, cur);
+    } else {
+        const int last = ngroups - 1;
+        for (int g = 0; g < ngroups; g += 2) {
+            load_group(min(g + 1, last), nxt);
+            compute(g, cur);
+            if (g + 1 > last) break;
+            load_group(min(g + 2, last), cur);
+            compute(g + 1, nxt);
+        }
+    }
+#endif
+}
+
+// One launch of the kernel for NT tokens per pass, token mode MODE and the
+// lane count chosen by the host.  Each (NT, MODE) pair is instantiated in one
+// of the gemv_valu_n*.hip translation units.
+template <int NT, int MODE>
+hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, unsigned grid, hipStream_t st) {
+    const size_t lds = (size_t)a.ntok * (size_t)a.K;
+    switch (lpr) {
+        case 8: hipLaunchKernelGGL((gemv_valu_kernel<NT, 8, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((gemv_valu_kernel<NT, 16, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((gemv_valu_kernel<NT, 32, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        default: hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+#define BITNET_GEMV_EXTERN(NT, MODE) \
+    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, unsigned, hipStream_t)
+// int8 tokens (mode 0) take at most two per pass; the fused modes up to eight
+BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);
+BITNET_GEMV_EXTERN(2, 0); BITNET_GEMV_EXTERN(2, 1); BITNET_GEMV_EXTERN(2, 2);
+BITNET_GEMV_EXTERN(4, 1); BITNET_GEMV_EXTERN(4, 2);
+BITNET_GEMV_EXTERN(8, 1); BITNET_GEMV_EXTERN(8, 2);
+#undef BITNET_GEMV_EXTERN
+
+}  // namespace bitnet

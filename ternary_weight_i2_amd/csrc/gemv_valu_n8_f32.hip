@@ -1,0 +1,7 @@
+// gemv_valu_n8_f32.hip -- decode GEMV kernels for 5-8 fp32 tokens per pass
+// (every lane count), compiled on their own so the units build in parallel.
+#include "gemv_valu.h"
+
+namespace bitnet {
+template hipError_t launch_gemv_nt<8, 1>(const GemvArgs &, int, unsigned, hipStream_t);
+}  // namespace bitnet

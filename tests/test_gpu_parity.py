@@ -353,3 +353,4 @@ def test_linear_large_sampled(bn, projs):
     M0 = min(Ms)
     rows = [(0, 32), (M0 // 2 + 3, 32), (M0 - 17, 17)]
     run_linear(bn, Ms, K, 1, "bf16", seed=K + len(projs), rows=rows, check_unfused=False)
+
