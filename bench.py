@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the secondary per-row measurements")
+    ap.add_argument("--only", choices=("pack", "quant", "decode", "large", "prefill"),
+                    help="run only this group of secondary rows and print them (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
                          "(calibrates HBM byte counters) and exit")
@@ -215,11 +217,21 @@ def _events_time(torch, fn, reps, warmup=3):
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
-def secondary_rows(bn, synth, torch, stack):
+def secondary_rows(bn, synth, torch, stack, only=None):
     """One figure per other hot-path row, each timed with HIP events on the
     launch stream.  Shapes are the workloads' own; weights reuse the decode
     stack where the shapes match (so they stream from HBM), else are drawn
-    fresh on the device."""
+    fresh on the device.  ``only`` picks one group of rows."""
+    rows = {}
+    parts = {"pack": row_pack, "quant": row_quant, "decode": row_decode,
+             "large": row_large, "prefill": row_prefill}
+    for name, fn in parts.items():
+        if only is None or only == name:
+            rows.update(fn(bn, synth, torch, stack))
+    return rows
+
+
+def row_pack(bn, synth, torch, stack):
     rows = {}
     # a1: pack (one-time step) -- 6912x2560 int8 -> I2_S
     M, K = synth.SHAPES["b2"]["gate"]
@@ -235,6 +247,11 @@ def secondary_rows(bn, synth, torch, stack):
                     "GB/s": round((M * K + M * K // 4) / t / 1e9, 1),
                     "note": "includes the stream sync that reads the bad-value count"}
     del W, out
+    return rows
+
+
+def row_quant(bn, synth, torch, stack):
+    rows = {}
     # a2: quantisation of a 4096x1024 bf16 prefill block
     N, K = 4096, 1024
     x = synth.tokens_bf16_torch(N, K, 12)
@@ -244,6 +261,11 @@ def secondary_rows(bn, synth, torch, stack):
     t = _events_time(torch, lambda: bn.quant_act(x, out=o), 50)
     rows["quant"] = {"shape": f"{N}x{K} bf16", "us": round(t * 1e6, 2),
                      "GB/s": round((N * K * 3 + N * 8) / t / 1e9, 1)}
+    return rows
+
+
+def row_decode(bn, synth, torch, stack):
+    rows = {}
     # a4: batched decode on the 2B stack shapes, N = 4, 16, 64 (weights from HBM)
     for N in (4, 16, 64):
         bufs = []
@@ -270,6 +292,11 @@ def secondary_rows(bn, synth, torch, stack):
                                 "TOPS": round(ops / t / 1e12, 3),
                                 "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
         del bufs, g
+    return rows
+
+
+def row_large(bn, synth, torch, stack):
+    rows = {}
     # a3 at streaming sizes: large layer (8 layers x 7 projections, 1.71 GB), N = 1 and 16
     large = []
     for l in range(8):
@@ -301,31 +328,56 @@ def secondary_rows(bn, synth, torch, stack):
                                "tokens_per_s": round(N / t, 1)}
         del bufs, g
     del large
-    # a5: prefill GEMM on the 0.6B-class projections, N = 128 and 4096
-    e06 = []
-    for p in synth.PROJ_NAMES:
-        M, K = synth.SHAPES["e06"][p]
-        W = synth.ternary_torch(M, K, synth.stack_seed("e06", 0, p, "weights"))
-        e06.append((bn.pack(W), synth.weight_scale(synth.rng_for("e06", 0, p, "scale")), M, K))
-        del W
-    for N in (128, 4096):
-        for outputs in ("y", "dot+y"):
-            bufs = []
-            for P, alpha, M, K in e06:
-                q = bn.quant_act(synth.tokens_bf16_torch(N, K, 19 + K))
-                d = torch.empty((N, M), dtype=torch.int32, device="cuda") if outputs != "y" else None
-                yy = torch.empty((N, M), dtype=torch.float32, device="cuda")
-                bufs.append((P, alpha, q, d, yy, M, K))
+    return rows
 
-            def run(bufs=bufs, outputs=outputs):
-                for P, alpha, q, d, yy, M, K in bufs:
-                    bn.gemm(P, alpha, q[0], q[1], q[2], want_dot=d is not None, out=(d, yy))
-            t = _events_time(torch, run, 20)
-            ops = sum(2 * M * K * N for P, a, q, d, yy, M, K in bufs)
-            rows[f"prefill_N{N}_{outputs}"] = {
-                "workload": "0.6B-class q/k/v/o/gate/up/down", "us": round(t * 1e6, 1),
-                "TOPS": round(ops / t / 1e12, 2),
+
+def row_prefill(bn, synth, torch, stack):
+    """a5: prefill GEMM on the 0.6B-class layer, N = 128 and 4096 tokens: one
+    grouped launch per group of projections sharing their input (q/k/v, o,
+    gate/up, down), tokens already quantised; plus the whole layer step through
+    bitnet_linear_i2s (quantiser + grouped GEMM) and the per-matrix launches."""
+    rows = {}
+    groups = []
+    for _, projs in GROUPS:
+        K = synth.SHAPES["e06"][projs[0]][1]
+        mats = []
+        for p in projs:
+            M, Kp = synth.SHAPES["e06"][p]
+            W = synth.ternary_torch(M, Kp, synth.stack_seed("e06", 0, p, "weights"))
+            mats.append((bn.pack(W), synth.weight_scale(synth.rng_for("e06", 0, p, "scale"))))
+            del W
+        groups.append((K, mats))
+    for N in (128, 4096):
+        xs = [synth.tokens_bf16_torch(N, K, 19 + K) for K, _ in groups]
+        qs = [bn.quant_act(x) for x in xs]
+        ops = sum(2 * P.shape[0] * K * N for K, mats in groups for P, _ in mats)
+        variants = [("y", False, "group"), ("dot+y", True, "group"), ("y_linear", False, "linear")]
+        if N == 4096:
+            variants.append(("y_per_matrix", False, "single"))
+        for tag, want_dot, how in variants:
+            outs = [[(torch.empty((N, P.shape[0]), dtype=torch.int32, device="cuda") if want_dot else None,
+                      torch.empty((N, P.shape[0]), dtype=torch.float32, device="cuda"))
+                     for P, _ in mats] for K, mats in groups]
+
+            def run(how=how, outs=outs):
+                for (K, mats), x, q, o in zip(groups, xs, qs, outs):
+                    if how == "group":
+                        bn.gemm_group(mats, q[0], q[1], q[2], out=o)
+                    elif how == "linear":
+                        bn.linear(x, mats, out=o, qout=q)
+                    else:
+                        for (P, a), (d, y) in zip(mats, o):
+                            bn.gemm(P, a, q[0], q[1], q[2], want_dot=d is not None, out=(d, y))
+            g = capture(torch, run)
+            t = time_graph(torch, g, 20, 3) / 20
+            del g
+            rows[f"prefill_N{N}_{tag}"] = {
+                "workload": "0.6B-class layer q/k/v/o/gate/up/down",
+                "launches": {"group": "4 grouped GEMM", "linear": "4 x (quantise + grouped GEMM)",
+                             "single": "7 GEMM"}[how],
+                "us": round(t * 1e6, 1), "TOPS": round(ops / t / 1e12, 2),
                 "mfma_frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)}
+            del outs
     return rows
 
 
@@ -345,6 +397,13 @@ def main():
     from ternary_weight_i2_amd import synth
     bn.load()
     torch.cuda.set_device(0)
+
+    if args.only:
+        # one group of secondary rows alone (for profiling); not the bench line
+        stack = build_stack(bn, synth, torch, args.layers) if args.only == "decode" else None
+        rows = secondary_rows(bn, synth, torch, stack, only=args.only)
+        print(json.dumps({"only": args.only, "rows": rows}), flush=True)
+        return
 
     stack = build_stack(bn, synth, torch, args.layers)
     torch.cuda.synchronize()

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define BITNET_ABI_VERSION 1
+#define BITNET_ABI_VERSION 2
 #define BITNET_MAX_K 32768          /* largest supported reduction length   */
 #define BITNET_GEMV_MAX_N 64        /* largest token count of the decode call */
 #define BITNET_GEMM_MAX_N (1 << 21) /* largest token count of the prefill call */
@@ -141,11 +141,15 @@ int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t M,
  *   xq, x_scale, x_sum   optional outputs (may be NULL when N <= 8): the
  *              quantised tokens exactly as bitnet_quant_act_i8 writes them.
  *              Required when N > 8 (they then carry the tokens between the
- *              quantiser and the MFMA kernel).
+ *              quantiser and the MFMA kernels).
  *
+ * N <= 8: one launch quantises and multiplies.  8 < N <= BITNET_GEMV_MAX_N:
+ * quantiser, then the batched-decode MFMA kernel per matrix.  Larger N
+ * (prefill): quantiser, then one grouped MFMA GEMM launch for all matrices.
  * Every output equals what bitnet_quant_act_i8 followed by
- * bitnet_gemv_i2s_i8 on each matrix produces, bit for bit.
- * 0 <= N <= BITNET_GEMV_MAX_N; 1 <= n_mats <= BITNET_MAX_GROUP.
+ * bitnet_gemv_i2s_i8 (N <= BITNET_GEMV_MAX_N) or bitnet_gemm_i2s_i8 on each
+ * matrix produces, bit for bit.
+ * 0 <= N <= BITNET_GEMM_MAX_N; 1 <= n_mats <= BITNET_MAX_GROUP.
  */
 typedef struct {
     const uint8_t *packed;
@@ -158,6 +162,26 @@ typedef struct {
 int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
                       const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq,
                       float *x_scale, int32_t *x_sum, void *stream);
+
+/*
+ * bitnet_gemm_i2s_i8_group -- prefill matmul of several I2_S matrices that
+ * share one block of quantised tokens, in one MFMA launch (e.g. q/k/v, or
+ * gate/up, of a layer).  [P1 §4-5 (a separate prefill path), §4-3 (one
+ * token block reused by every weight row); P2 §3; P3 §3.2]
+ *
+ *   mats     host array of n_mats descriptors (1 <= n_mats <=
+ *            BITNET_MAX_GROUP), read during the call only: packed [M][K/4]
+ *            I2_S (16-byte aligned), M, w_scale, outputs dot [N][M] int32 /
+ *            y [N][M] fp32 (either may be NULL, not both, unless M == 0).
+ *   xq, x_scale, x_sum   the tokens as bitnet_quant_act_i8 writes them
+ *            (xq 16-byte aligned).
+ *
+ * Outputs equal bitnet_gemm_i2s_i8 on each matrix, bit for bit.
+ * 0 <= N <= BITNET_GEMM_MAX_N; N == 0 or all M == 0 is a no-op.
+ */
+int bitnet_gemm_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
+                             const int8_t *xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t N, void *stream);
 
 /* Thread-local description of the last non-OK status on this thread
  * (empty string if none).  The pointer stays valid until the next call on

@@ -60,6 +60,9 @@ def load() -> ctypes.CDLL:
     L.bitnet_linear_i2s.argtypes = [p, ctypes.c_int, i64, i64, ctypes.POINTER(I2SMatrix),
                                     ctypes.c_int, p, p, p, p]
     L.bitnet_linear_i2s.restype = ctypes.c_int
+    L.bitnet_gemm_i2s_i8_group.argtypes = [ctypes.POINTER(I2SMatrix), ctypes.c_int, i64, p, p, p,
+                                           i64, p]
+    L.bitnet_gemm_i2s_i8_group.restype = ctypes.c_int
     for fn in ("bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
                "bitnet_gemm_i2s_i8", "bitnet_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
@@ -154,10 +157,40 @@ def gemm(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=No
                    x_sum, want_dot, want_y, out)
 
 
+def _mats_out(mats, N, device, want_dot, want_y, out):
+    import torch
+    if out is not None:
+        return out
+    res = []
+    for P, _ in mats:
+        M = P.shape[0]
+        res.append((torch.empty((N, M), dtype=torch.int32, device=device) if want_dot else None,
+                    torch.empty((N, M), dtype=torch.float32, device=device) if want_y else None))
+    return res
+
+
+def _mat_array(mats, out):
+    arr = (I2SMatrix * len(mats))()
+    for i, ((P, ws), (d, y)) in enumerate(zip(mats, out)):
+        arr[i] = I2SMatrix(_ptr(P), P.shape[0], float(ws), _ptr(d), _ptr(y))
+    return arr
+
+
+def gemm_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
+    """Prefill matmul of every (packed, w_scale) in ``mats`` by the same
+    quantised tokens, one MFMA launch -> [(dot | None, y | None) per matrix]."""
+    N, K = xq.shape
+    out = _mats_out(mats, N, xq.device, want_dot, want_y, out)
+    _check(load().bitnet_gemm_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
+                                           _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
+    return out
+
+
 def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
-    """Fused decode linear: quantise tokens x[N][K] (fp32/bf16, cuda) and multiply
-    them by every (packed, w_scale) in ``mats`` in one launch (N <= 8; for
-    N > 8 the library quantises into ``qout`` first, allocated here if None).
+    """Linear layer step: quantise tokens x[N][K] (fp32/bf16, cuda) and multiply
+    them by every (packed, w_scale) in ``mats`` -- one fused launch for N <= 8;
+    for N > 8 the library quantises into ``qout`` first (allocated here if
+    None), then runs the batched-decode (N <= 64) or grouped prefill kernels.
 
     Returns ([(dot | None, y | None) per matrix], (xq, s, xsum) | None)."""
     import torch
@@ -167,20 +200,12 @@ def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
     if dt is None:
         raise TypeError("x must be float32 or bfloat16")
     N, K = x.shape
-    if out is None:
-        out = []
-        for P, _ in mats:
-            M = P.shape[0]
-            out.append((torch.empty((N, M), dtype=torch.int32, device=x.device) if want_dot else None,
-                        torch.empty((N, M), dtype=torch.float32, device=x.device) if want_y else None))
+    out = _mats_out(mats, N, x.device, want_dot, want_y, out)
     if qout is None and N > 8:
         qout = (torch.empty((N, K), dtype=torch.int8, device=x.device),
                 torch.empty((N,), dtype=torch.float32, device=x.device),
                 torch.empty((N,), dtype=torch.int32, device=x.device))
-    arr = (I2SMatrix * len(mats))()
-    for i, ((P, ws), (d, y)) in enumerate(zip(mats, out)):
-        arr[i] = I2SMatrix(_ptr(P), P.shape[0], float(ws), _ptr(d), _ptr(y))
     xq, xs, xsum = qout if qout is not None else (None, None, None)
-    _check(load().bitnet_linear_i2s(_ptr(x), dt, N, K, arr, len(mats), _ptr(xq), _ptr(xs),
-                                    _ptr(xsum), _stream(x)))
+    _check(load().bitnet_linear_i2s(_ptr(x), dt, N, K, _mat_array(mats, out), len(mats),
+                                    _ptr(xq), _ptr(xs), _ptr(xsum), _stream(x)))
     return out, qout

@@ -176,26 +176,19 @@ BITNET_API int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
     if (int s = check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, BITNET_GEMM_MAX_N, dot, y))
         return s;
     if (M == 0 || N == 0) return ok();
-    hipError_t e = bitnet::launch_gemm_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot,
-                                            y, static_cast<hipStream_t>(stream));
+    const bitnet::GemmMat m{packed, dot, y, w_scale, (int)M, 0};
+    hipError_t e = bitnet::launch_gemm_mfma(&m, 1, K, xq, x_scale, x_sum, N,
+                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("bitnet_gemm_i2s_i8: launch", e);
     return ok();
 }
 
-static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int64_t K,
-                       const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq, float *x_scale,
-                       int32_t *x_sum, void *stream) {
-    if (dtype != BITNET_F32 && dtype != BITNET_BF16)
-        return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
-    if (N < 0 || N > BITNET_GEMV_MAX_N)
-        return fail(BITNET_E_SHAPE, "%s: N=%lld outside [0, %d]", fn, (long long)N,
-                    BITNET_GEMV_MAX_N);
-    if (int s = check_k(fn, K)) return s;
+// Validate a host array of matrix descriptors (shared by the grouped calls).
+static int check_mats(const char *fn, const bitnet_i2s_matrix *mats, int n_mats) {
     if (n_mats < 1 || n_mats > BITNET_MAX_GROUP)
         return fail(BITNET_E_SHAPE, "%s: n_mats=%d outside [1, %d]", fn, n_mats,
                     BITNET_MAX_GROUP);
     if (!mats) return fail(BITNET_E_NULL, "%s: mats is NULL", fn);
-    bitnet::GemvMat gm[bitnet::kMaxMats];
     for (int i = 0; i < n_mats; ++i) {
         const bitnet_i2s_matrix &m = mats[i];
         if (m.M < 0 || m.M > 0x7fffffffLL)
@@ -209,8 +202,51 @@ static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int6
             if ((m.dot && !aligned(m.dot, 4)) || (m.y && !aligned(m.y, 4)))
                 return fail(BITNET_E_ALIGN, "%s: mats[%d] outputs must be 4-byte aligned", fn, i);
         }
-        gm[i] = bitnet::GemvMat{m.packed, m.dot, m.y, m.w_scale, (int)m.M, 0};
     }
+    return BITNET_OK;
+}
+
+BITNET_API int bitnet_gemm_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
+                                        const int8_t *xq, const float *x_scale,
+                                        const int32_t *x_sum, int64_t N, void *stream) {
+    const char *fn = "bitnet_gemm_i2s_i8_group";
+    if (int s = check_mats(fn, mats, n_mats)) return s;
+    if (N < 0 || N > BITNET_GEMM_MAX_N)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld outside [0, %d]", fn, (long long)N,
+                    BITNET_GEMM_MAX_N);
+    if (int s = check_k(fn, K)) return s;
+    bitnet::GemmMat gm[bitnet::kMaxMats];
+    int64_t rows = 0;
+    for (int i = 0; i < n_mats; ++i) {
+        gm[i] = bitnet::GemmMat{mats[i].packed, mats[i].dot, mats[i].y, mats[i].w_scale,
+                                (int)mats[i].M, 0};
+        rows += mats[i].M;
+    }
+    if (N == 0 || rows == 0) return ok();
+    if (!xq || !x_scale || !x_sum)
+        return fail(BITNET_E_NULL, "%s: xq, x_scale and x_sum are required", fn);
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+        return fail(BITNET_E_ALIGN, "%s: xq must be 16-byte and x_scale/x_sum 4-byte aligned", fn);
+    hipError_t e = bitnet::launch_gemm_mfma(gm, n_mats, K, xq, x_scale, x_sum, N,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int64_t K,
+                       const bitnet_i2s_matrix *mats, int n_mats, int8_t *xq, float *x_scale,
+                       int32_t *x_sum, void *stream) {
+    if (dtype != BITNET_F32 && dtype != BITNET_BF16)
+        return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (N < 0 || N > BITNET_GEMM_MAX_N)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld outside [0, %d]", fn, (long long)N,
+                    BITNET_GEMM_MAX_N);
+    if (int s = check_k(fn, K)) return s;
+    if (int s = check_mats(fn, mats, n_mats)) return s;
+    bitnet::GemvMat gm[bitnet::kMaxMats];
+    for (int i = 0; i < n_mats; ++i)
+        gm[i] = bitnet::GemvMat{mats[i].packed, mats[i].dot, mats[i].y, mats[i].w_scale,
+                                (int)mats[i].M, 0};
     if (N == 0) return ok();
     if (!x) return fail(BITNET_E_NULL, "%s: x is NULL", fn);
     if (!aligned(x, 16) || (xq && !aligned(xq, 16)) || (x_scale && !aligned(x_scale, 4)) ||
@@ -223,12 +259,20 @@ static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int6
     if (N <= 8) {
         e = bitnet::launch_gemv_valu(gm, n_mats, K, N, dtype == BITNET_BF16 ? 2 : 1, x, nullptr,
                                      nullptr, xq, x_scale, x_sum, st);
-    } else {
+    } else if (N <= BITNET_GEMV_MAX_N) {
         e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
         for (int i = 0; i < n_mats && e == hipSuccess; ++i)
             if (gm[i].M > 0)
                 e = bitnet::launch_gemv_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
                                              x_sum, N, gm[i].dot, gm[i].y, st);
+    } else {
+        e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
+        if (e == hipSuccess) {
+            bitnet::GemmMat mm[bitnet::kMaxMats];
+            for (int i = 0; i < n_mats; ++i)
+                mm[i] = bitnet::GemmMat{gm[i].packed, gm[i].dot, gm[i].y, gm[i].alpha, gm[i].M, 0};
+            e = bitnet::launch_gemm_mfma(mm, n_mats, K, xq, x_scale, x_sum, N, st);
+        }
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();

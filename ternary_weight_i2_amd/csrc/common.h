@@ -150,9 +150,28 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
 hipError_t launch_gemv_mfma(const uint8_t *packed, float alpha, int64_t M, int64_t K,
                             const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
                             int32_t *dot, float *y, hipStream_t st);
-hipError_t launch_gemm_mfma(const uint8_t *packed, float alpha, int64_t M,
-                            int64_t K, const int8_t *xq, const float *xs,
-                            const int32_t *xsum, int64_t N, int32_t *dot,
-                            float *y, hipStream_t st);
+// Prefill launch over up to kMaxMats matrices that share K and the tokens;
+// output tiles [tile_begin, next tile_begin) belong to matrix i.
+struct GemmMat {
+    const uint8_t *packed;
+    int32_t *dot;
+    float *y;
+    float alpha;
+    int M;
+    int tile_begin;
+};
+struct GemmArgs {
+    GemmMat mat[kMaxMats];
+    int nmats;
+    int K;
+    int N;
+    const int8_t *xq;
+    const float *xs;
+    const int32_t *xsum;
+};
+// Prefill (any token count) on int8 MFMA: every matrix of `mats` (M > 0)
+// times the same quantised tokens, in one launch.
+hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
+                            const float *xs, const int32_t *xsum, int64_t N, hipStream_t st);
 
 }  // namespace bitnet

@@ -38,11 +38,7 @@ namespace bitnet {
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 template <int BM, int BN, int WM, int WN, int kStages>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
-    const uint8_t *__restrict__ packed, float alpha, int M, int K,
-    const int8_t *__restrict__ xq, const float *__restrict__ xs,
-    const int32_t *__restrict__ xsum, int N, int32_t *__restrict__ dot,
-    float *__restrict__ y) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs a) {
     static_assert(kStages >= 2, "at least double buffering");
     constexpr int NW = WM * WN;        // waves per workgroup
     constexpr int MI = BM / WM / 32;   // 32-row MFMA tiles per wave
@@ -65,13 +61,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
     // (id % 8); renumbering so that each XCD gets a contiguous run of tiles,
     // M-tile fastest, makes the workgroups of one XCD share token tiles in its
     // L2 instead of every XCD fetching every token tile.
-    const int mtiles = (M + BM - 1) / BM;
+    // Tiles are numbered matrix by matrix, M-tile fastest.
     const int total = (int)gridDim.x;
     int id = (int)blockIdx.x;
 #if BITNET_GEMM_XCD_REMAP
     if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
 #endif
-    const int m0 = (id % mtiles) * BM, n0 = (id / mtiles) * BN;
+    int mat = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMats; ++i)
+        if (i < a.nmats && id >= a.mat[i].tile_begin) mat = i;
+    const uint8_t *__restrict__ packed = a.mat[mat].packed;
+    int32_t *__restrict__ dot = a.mat[mat].dot;
+    float *__restrict__ y = a.mat[mat].y;
+    const float alpha = a.mat[mat].alpha;
+    const int M = a.mat[mat].M, K = a.K, N = a.N;
+    const int8_t *__restrict__ xq = a.xq;
+    const float *__restrict__ xs = a.xs;
+    const int32_t *__restrict__ xsum = a.xsum;
+    const int local = id - a.mat[mat].tile_begin;
+    const int mtiles = (M + BM - 1) / BM;
+    const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * BN;
     const int64_t rowb = K >> 2;
     const int nkb = K / kBlock;
 
@@ -193,23 +203,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(
 }
 
 template <int BM, int BN, int WM, int WN, int S>
-static hipError_t run_gemm(const uint8_t *packed, float alpha, int64_t M, int64_t K,
-                           const int8_t *xq, const float *xs, const int32_t *xsum,
-                           int64_t N, int32_t *dot, float *y, hipStream_t st) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, S>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0,
-                       st, packed, alpha, (int)M, (int)K, xq, xs, xsum, (int)N, dot, y);
+static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
+                           const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
+    GemmArgs a{};
+    const int64_t ntiles = (N + BN - 1) / BN;
+    int64_t tiles = 0;
+    int n = 0;
+    for (int i = 0; i < nmats; ++i) {
+        if (mats[i].M <= 0) continue;
+        a.mat[n] = mats[i];
+        a.mat[n].tile_begin = (int)tiles;
+        tiles += ((mats[i].M + BM - 1) / BM) * ntiles;
+        ++n;
+    }
+    if (n == 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;   // tile ids are int
+    a.nmats = n;
+    a.K = (int)K;
+    a.N = (int)N;
+    a.xq = xq;
+    a.xs = xs;
+    a.xsum = xsum;
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, S>), dim3((unsigned)tiles), dim3(WM * WN * 64),
+                       0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_mfma(const uint8_t *packed, float alpha, int64_t M,
-                            int64_t K, const int8_t *xq, const float *xs,
-                            const int32_t *xsum, int64_t N, int32_t *dot,
-                            float *y, hipStream_t st) {
+hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
+                            const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
     // token tile matched to small N so no MFMA column work is wasted
-    if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
-    if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
-    return run_gemm<128, 128, 2, 2, 4>(packed, alpha, M, K, xq, xs, xsum, N, dot, y, st);
+    if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    return run_gemm<128, 128, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
 }  // namespace bitnet

@@ -34,8 +34,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = set(declared_functions())
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
-            "bitnet_gemm_i2s_i8", "bitnet_linear_i2s", "bitnet_last_error",
-            "bitnet_abi_version"} <= fns
+            "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_linear_i2s",
+            "bitnet_last_error", "bitnet_abi_version"} <= fns
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -124,7 +124,8 @@ def test_linear_validation(L):
     good = I2SMatrix(FAKE, 64, 0.1, FAKE, FAKE)
     g1 = mats(good)
     assert f(FAKE, 5, 1, 256, g1, 1, None, None, None, None) == E_DTYPE
-    assert f(FAKE, 1, 65, 256, g1, 1, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, (1 << 21) + 1, 256, g1, 1, None, None, None, None) == E_SHAPE
+    assert f(FAKE, 1, 65, 256, g1, 1, None, None, None, None) == E_NULL   # prefill needs xq
     assert f(FAKE, 1, -1, 256, g1, 1, None, None, None, None) == E_SHAPE
     assert f(FAKE, 1, 1, 200, g1, 1, None, None, None, None) == E_SHAPE
     assert f(FAKE, 1, 1, 256, g1, 0, None, None, None, None) == E_SHAPE
@@ -147,6 +148,44 @@ def test_linear_validation(L):
     assert f(None, 1, 0, 256, g1, 1, None, None, None, None) == OK
     assert f(None, 1, 0, 256, mats(I2SMatrix(None, 0, 0.1, None, None)), 1,
              None, None, None, None) == OK
+
+
+def test_gemm_group_validation(L):
+    from ternary_weight_i2_amd._binding import I2SMatrix
+    f = L.bitnet_gemm_i2s_i8_group
+
+    def mats(*ms):
+        arr = (I2SMatrix * len(ms))()
+        for i, m in enumerate(ms):
+            arr[i] = m
+        return arr
+    good = I2SMatrix(FAKE, 64, 0.1, FAKE, FAKE)
+    g1 = mats(good)
+    assert f(g1, 0, 256, FAKE, FAKE, FAKE, 4, None) == E_SHAPE
+    assert f(mats(*[good] * 9), 9, 256, FAKE, FAKE, FAKE, 4, None) == E_SHAPE
+    assert f(None, 1, 256, FAKE, FAKE, FAKE, 4, None) == E_NULL
+    assert f(g1, 1, 200, FAKE, FAKE, FAKE, 4, None) == E_SHAPE
+    assert f(g1, 1, 256, FAKE, FAKE, FAKE, -1, None) == E_SHAPE
+    assert f(g1, 1, 256, FAKE, FAKE, FAKE, (1 << 21) + 1, None) == E_SHAPE
+    assert f(g1, 1, 256, None, FAKE, FAKE, 4, None) == E_NULL
+    assert f(g1, 1, 256, FAKE, None, FAKE, 4, None) == E_NULL
+    assert f(g1, 1, 256, MIS, FAKE, FAKE, 4, None) == E_ALIGN
+    assert f(g1, 1, 256, FAKE, FAKE + 2, FAKE, 4, None) == E_ALIGN
+    assert f(mats(good, I2SMatrix(None, 64, 0.1, FAKE, FAKE)), 2, 256, FAKE, FAKE, FAKE, 4,
+             None) == E_NULL
+    assert f(mats(I2SMatrix(FAKE, 64, 0.1, None, None)), 1, 256, FAKE, FAKE, FAKE, 4,
+             None) == E_NULL
+    assert f(mats(I2SMatrix(MIS, 64, 0.1, FAKE, FAKE)), 1, 256, FAKE, FAKE, FAKE, 4,
+             None) == E_ALIGN
+    assert f(mats(I2SMatrix(FAKE, 64, 0.1, FAKE + 1, None)), 1, 256, FAKE, FAKE, FAKE, 4,
+             None) == E_ALIGN
+    assert f(mats(I2SMatrix(FAKE, -2, 0.1, FAKE, FAKE)), 1, 256, FAKE, FAKE, FAKE, 4,
+             None) == E_SHAPE
+    assert "bitnet_gemm_i2s_i8_group" in _err(L)
+    # no-ops: N == 0, or every matrix empty
+    assert f(g1, 1, 256, None, None, None, 0, None) == OK
+    assert f(mats(I2SMatrix(None, 0, 0.1, None, None)), 1, 256, None, None, None, 4, None) == OK
+    assert _err(L) == ""
 
 
 def test_last_error_is_per_thread(L):

@@ -305,7 +305,8 @@ def run_linear(bn, Ms, K, N, dtype, seed, rows=None, outliers=False, check_unfus
         M = W.shape[0]
         dn, yn = d.cpu().numpy(), y.cpu().numpy()
         if check_unfused and M > 0:
-            d2, y2 = bn.gemv(P, alpha, xq, xs, xsum)
+            unfused = bn.gemv if N <= 64 else bn.gemm
+            d2, y2 = unfused(P, alpha, xq, xs, xsum)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(dn, d2.cpu().numpy())
             np.testing.assert_array_equal(yn.view(np.uint32), y2.cpu().numpy().view(np.uint32))
@@ -321,6 +322,7 @@ def run_linear(bn, Ms, K, N, dtype, seed, rows=None, outliers=False, check_unfus
 LINEAR_CASES = [((7,), 128, 1, "f32"), ((64, 0, 17), 256, 2, "bf16"),
                 ((130, 33, 65), 384, 5, "bf16"), ((100,), 640, 8, "f32"),
                 ((70, 70), 896, 9, "bf16"), ((65,), 384, 64, "bf16"),
+                ((130, 0, 33), 384, 65, "bf16"), ((200, 129), 640, 300, "f32"),
                 ((3, 5, 7, 9, 11, 13, 15, 17), 512, 3, "bf16"), ((40,), 32768, 2, "f32"),
                 ((300,), 8192, 8, "bf16"), ((129,), 28672, 3, "bf16")]
 
@@ -354,3 +356,63 @@ def test_linear_large_sampled(bn, projs):
     rows = [(0, 32), (M0 // 2 + 3, 32), (M0 - 17, 17)]
     run_linear(bn, Ms, K, 1, "bf16", seed=K + len(projs), rows=rows, check_unfused=False)
 
+
+def run_gemm_group(bn, Ms, K, N, seed, rows=None, want_dot=True):
+    """Grouped prefill GEMM vs the oracle (sampled rows) and vs bitnet_gemm_i2s_i8
+    on each matrix (bit for bit, every row)."""
+    rng = np.random.default_rng(seed)
+    Ws = [synth.ternary(rng, M, K) for M in Ms]
+    alphas = [synth.weight_scale(rng) for _ in Ms]
+    x = synth.tokens_bf16(rng, N, K)
+    xq, xs, xsum = bn.quant_act(to_bf16_tensor(x))
+    Ps = [bn.pack(dev(W)) for W in Ws]
+    outs = bn.gemm_group(list(zip(Ps, alphas)), xq, xs, xsum, want_dot=want_dot)
+    torch.cuda.synchronize()
+    q, s, qs = oracle.quant_act(x)
+    for W, P, alpha, (d, y) in zip(Ws, Ps, alphas, outs):
+        M = W.shape[0]
+        if M == 0:
+            continue
+        d2, y2 = bn.gemm(P, alpha, xq, xs, xsum)
+        torch.cuda.synchronize()
+        yn = y.cpu().numpy()
+        np.testing.assert_array_equal(yn.view(np.uint32), y2.cpu().numpy().view(np.uint32))
+        if want_dot:
+            np.testing.assert_array_equal(d.cpu().numpy(), d2.cpu().numpy())
+        else:
+            assert d is None
+        for r0, nr in (rows if rows is not None else [(0, M)]):
+            Pr, _ = oracle.pack_i2s(W[r0:r0 + nr])
+            D, _ = oracle.linear_i2s(Pr, K, q, s, alpha, nthreads=8, want_y=False)
+            if want_dot:
+                np.testing.assert_array_equal(d.cpu().numpy()[:, r0:r0 + nr], D)
+            check_y(yn[:, r0:r0 + nr], D, alpha, s)
+
+
+@pytest.mark.parametrize("Ms,K,N", [((5,), 128, 1), ((130, 0, 33), 384, 65),
+                                    ((128, 256, 384), 512, 128), ((300, 7), 640, 300),
+                                    ((1, 2, 3, 4, 5, 6, 7, 8), 256, 40)])
+def test_gemm_group_small(bn, Ms, K, N):
+    run_gemm_group(bn, Ms, K, N, seed=sum(Ms) + K + N)
+
+
+@pytest.mark.parametrize("group", ["attn", "ffn"])
+@pytest.mark.parametrize("N", [128, 4096])
+def test_gemm_group_e06_prefill(bn, group, N):
+    """The benchmark's prefill launches: q/k/v and gate/up of the 0.6B-class
+    layer in one launch each, sampled rows against the oracle."""
+    projs = {"attn": ("q", "k", "v"), "ffn": ("gate", "up")}[group]
+    Ms = [synth.SHAPES["e06"][p][0] for p in projs]
+    K = synth.SHAPES["e06"][projs[0]][1]
+    rows = [(0, 40), (min(Ms) // 2 + 5, 33), (min(Ms) - 19, 19)]
+    run_gemm_group(bn, Ms, K, N, seed=N + len(group), rows=rows, want_dot=(N == 128))
+
+
+def test_linear_e06_prefill_layer(bn):
+    """The 0.6B-class layer's four prefill calls through bitnet_linear_i2s
+    (quantise + grouped GEMM), N=256, sampled rows against the oracle."""
+    for projs in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        Ms = [synth.SHAPES["e06"][p][0] for p in projs]
+        K = synth.SHAPES["e06"][projs[0]][1]
+        run_linear(bn, Ms, K, 256, "bf16", seed=K + len(projs),
+                   rows=[(0, 24), (min(Ms) - 24, 24)])
