@@ -6,27 +6,31 @@
 //
 // Tiling: a workgroup of WM x WN waves computes a BM x BN tile of the output
 // (weight rows x tokens); wave (wm, wn) owns a (32*MI) x (32*NJ) sub-tile made
-// of 32x32 MFMA tiles.  K advances one 128-weight I2_S block at a time.
-// Tiles are sized so every wave issues whole 1 KB DMA instructions per block.
+// of 32x32 MFMA tiles.  K advances one 128-weight I2_S block at a time.  One
+// launch may serve several matrices that share the tokens (tiles numbered
+// matrix by matrix).
 //
 // Operand layout.  For MFMA step s of a block (32 k each, s = 0..3) lane
 // (r, kg) -- r = lane%32, kg = lane/32 -- supplies 16 bytes for k = 32s + 16kg
 // + 0..15 of row/token r.  The B operand (tokens) is therefore a plain
-// 16-byte copy of the token row, and the tokens are staged in LDS in their
-// natural order (with an XOR swizzle of the 16-byte pieces inside a row so a
-// wave's reads spread over the banks).  The contraction is order-free, so the A operand is built to match:
-// those 16 positions are the 2-bit field s of the 16 packed bytes of half kg
-// of the row's block.  One 16-byte weight load per lane per block serves all
-// four steps (shift by 6-2s and mask per dword, no shuffle).  Weights are read
-// straight from global memory (they are small and shared through L2); tokens
-// go through LDS because all waves of a column share them.
+// 16-byte copy of the token row; tokens are staged in LDS in their natural
+// order, with an XOR swizzle of the 16-byte pieces inside a row so a wave's
+// reads spread over the banks.  The contraction is order-free, so the A
+// operand is built to match: those 16 positions are the 2-bit field s of the
+// 16 packed bytes of half kg of the row's block.  One 16-byte read of the
+// packed weight tile per lane per block serves all four steps (shift by 6-2s
+// and mask per dword, no shuffle); the weights are never re-laid out.
 //
-// Pipelining: weight and token tiles move global -> LDS with the gfx950
-// LDS-DMA loads (global_load_lds_dwordx4: each lane's 16 bytes land at
-// M0 + 16*lane), three block stages deep, so no registers carry staged data
-// and the MFMAs of block kb overlap the loads of blocks kb+1 and kb+2; one
-// barrier per block.  Accumulators hold the raw-code sum R; the epilogue
-// writes D = R - sum(x) and y = D * alpha / s.
+// Pipelining: the packed weight tile (BM x 32 bytes) and the token tile
+// (BN x 128 bytes) of a block move global -> LDS with the gfx950 LDS-DMA loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16*lane; the
+// 1 KB instructions are dealt to the waves round-robin), kStages-1 blocks in
+// flight, so no registers carry staged data and the MFMAs of block kb overlap
+// the loads of the next blocks; one barrier per block.  Accumulators hold the
+// raw-code sum R; the epilogue writes D = R - sum(x) and y = D * (alpha / s),
+// the factor computed once per token before the main loop (two fp32
+// roundings, as D * alpha / s has; a division per output made the epilogue
+// VALU-bound).
 #include "common.h"
 
 namespace bitnet {
@@ -44,11 +48,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     constexpr int MI = BM / WM / 32;   // 32-row MFMA tiles per wave
     constexpr int NJ = BN / WN / 32;   // 32-token MFMA tiles per wave
     static_assert(MI >= 1 && NJ >= 1, "tile too small");
-    // LDS-DMA instructions per wave per block: each moves 64 lanes x 16 bytes.
-    constexpr int IA = BM / (32 * NW);  // weight tile: BM rows x 32 bytes
-    constexpr int IB = BN / (8 * NW);   // token tile: BN rows x 128 bytes
-    static_assert(IA >= 1 && IB >= 1 && BM % (32 * NW) == 0 && BN % (8 * NW) == 0,
-                  "tile shape: whole 1 KB DMA instructions per wave");
+    // LDS-DMA instructions per block (each moves 64 lanes x 16 bytes = 1 KB):
+    // TA for the weight tile (BM rows x 32 bytes), TB for the token tile (BN
+    // rows x 128 bytes), dealt to the waves round-robin: wave w issues
+    // instructions w, w + NW, ...; CMAX or CMIN of them.
+    constexpr int TA = BM / 32, TB = BN / 8, T = TA + TB;
+    static_assert(BM % 32 == 0 && BN % 8 == 0, "tile shape: whole 1 KB DMA instructions");
+    constexpr int CMAX = (T + NW - 1) / NW, CMIN = T / NW;
+    static_assert(CMIN >= 1, "every wave issues at least one DMA per block");
     constexpr int A_BYTES = BM * kBlockBytes, B_BYTES = BN * kBlock;
     constexpr int STAGE = A_BYTES + B_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * STAGE];
@@ -85,33 +92,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     const int64_t rowb = K >> 2;
     const int nkb = K / kBlock;
 
-    // Global source of this lane's 16 bytes in each DMA instruction.  Rows and
-    // tokens past the matrix are clamped to the last valid one (their results
-    // are never stored).  Token rows are XOR-swizzled: LDS slot c' of row r
-    // holds piece c' ^ (r & 7), which spreads a wave's B reads over the banks.
-    const uint8_t *asrc[IA];
+    // Global source of this lane's 16 bytes in each of the wave's DMA
+    // instructions (byte offset 1024*j of the stage; A first, then B).  Rows
+    // and tokens past the matrix are clamped to the last valid one (their
+    // results are never stored).  Token rows are XOR-swizzled: LDS slot c' of
+    // row r holds piece c' ^ (r & 7), which spreads a wave's B reads over the
+    // banks.
+    const bool full = wave < T - CMIN * NW;   // this wave issues CMAX, else CMIN
+    const int8_t *src[CMAX];
+    int64_t step[CMAX];                       // source advance per block
 #pragma unroll
-    for (int i = 0; i < IA; ++i) {
-        const int row = 32 * (wave * IA + i) + (lane >> 1);
-        asrc[i] = packed + (int64_t)min(m0 + row, M - 1) * rowb + 16 * (lane & 1);
-    }
-    const int8_t *bsrc[IB];
-#pragma unroll
-    for (int i = 0; i < IB; ++i) {
-        const int row = 8 * (wave * IB + i) + (lane >> 3);
-        const int piece = (lane & 7) ^ (row & 7);
-        bsrc[i] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
+    for (int c = 0; c < CMAX; ++c) {
+        const int j = min(wave + NW * c, T - 1);
+        if (j < TA) {
+            const int row = 32 * j + (lane >> 1);
+            src[c] = reinterpret_cast<const int8_t *>(packed) +
+                     (int64_t)min(m0 + row, M - 1) * rowb + 16 * (lane & 1);
+            step[c] = kBlockBytes;
+        } else {
+            const int row = 8 * (j - TA) + (lane >> 3);
+            const int piece = (lane & 7) ^ (row & 7);
+            src[c] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
+            step[c] = kBlock;
+        }
     }
     auto issue = [&](int kb, int st) {
         const int8_t *base = lds + st * STAGE;
 #pragma unroll
-        for (int i = 0; i < IA; ++i)
-            dma16(asrc[i] + (int64_t)kb * kBlockBytes, lds_addr_of(base + 1024 * (wave * IA + i)));
-#pragma unroll
-        for (int i = 0; i < IB; ++i)
-            dma16(bsrc[i] + (int64_t)kb * kBlock,
-                  lds_addr_of(base + A_BYTES + 1024 * (wave * IB + i)));
+        for (int c = 0; c < CMAX; ++c)
+            if (c < CMIN || full)
+                dma16(src[c] + (int64_t)kb * step[c], lds_addr_of(base + 1024 * (wave + NW * c)));
     };
+    // wait until this wave's DMAs of the oldest pending block have landed
+    auto wait_block = [&]() {
+        if (full) wait_vmcnt<CMAX * (kStages - 2)>();
+        else wait_vmcnt<CMIN * (kStages - 2)>();
+    };
+
+    // Per-token epilogue inputs, loaded before the main loop so their latency
+    // is hidden: sum(x) and the output factor alpha / s of each column.
+    int sxv[NJ];
+    float cfac[NJ];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int nc = min(n0 + (wn * NJ + nj) * 32 + r32, N - 1);
+        sxv[nj] = xsum[nc];
+        cfac[nj] = alpha / xs[nc];
+    }
 
     v16i acc[MI][NJ];
 #pragma unroll
@@ -127,35 +154,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
 #pragma unroll
     for (int p = 0; p < kStages - 1; ++p) issue(min(p, nkb - 1), p);
     for (int kb = 0; kb < nkb; ++kb) {
-        wait_vmcnt<(IA + IB) * (kStages - 2)>();
+        wait_block();
         __syncthreads();   // every wave's share of block kb is in LDS; stage (kb-1) is free
         issue(min(kb + kStages - 1, nkb - 1), (kb + kStages - 1) % kStages);
         const int8_t *sa = lds + (kb % kStages) * STAGE;
         const int8_t *sb = sa + A_BYTES;
-        v4i a[MI];
+        // All of the block's fragments are read from LDS up front (one LDS
+        // round trip), then the 4*MI*NJ MFMAs run back to back while the next
+        // step's codes are unpacked.
+        v4i a[MI], bf[4][NJ];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
             a[mi] = *reinterpret_cast<const v4i *>(sa + ((wm * MI + mi) * 32 + r32) * kBlockBytes +
                                                    16 * kg);
 #pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj) {
+                const int row = (wn * NJ + nj) * 32 + r32;
+                bf[s][nj] = *reinterpret_cast<const v4i *>(
+                    sb + row * kBlock + 16 * ((2 * s + kg) ^ (row & 7)));
+            }
+#pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int sh = 6 - 2 * s;
-            v4i af[MI], bf[NJ];
+            v4i af[MI];
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
                 af[mi] = v4i{(a[mi].x >> sh) & 0x03030303, (a[mi].y >> sh) & 0x03030303,
                              (a[mi].z >> sh) & 0x03030303, (a[mi].w >> sh) & 0x03030303};
 #pragma unroll
-            for (int nj = 0; nj < NJ; ++nj) {
-                const int row = (wn * NJ + nj) * 32 + r32;
-                bf[nj] = *reinterpret_cast<const v4i *>(
-                    sb + row * kBlock + 16 * ((2 * s + kg) ^ (row & 7)));
-            }
-#pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int nj = 0; nj < NJ; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[nj],
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[s][nj],
                                                                         acc[mi][nj], 0, 0, 0);
         }
     }
@@ -170,8 +202,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     for (int nj = 0; nj < NJ; ++nj) {
         const int n = n0 + (wn * NJ + nj) * 32 + r32;
         if (n >= N) continue;
-        const int sx = xsum[n];
-        const float s = xs[n];
+        const int sx = sxv[nj];
+        const float c = cfac[nj];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -182,7 +214,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     d[j] = acc[mi][nj][4 * q + j] - sx;
-                    yv[j] = ((float)d[j] * alpha) / s;
+                    yv[j] = (float)d[j] * c;
                 }
                 const int64_t o = (int64_t)n * M + mb;
                 if (vec_ok && mb + 3 < M) {
@@ -231,7 +263,10 @@ static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8
 
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    // token tile matched to small N so no MFMA column work is wasted
+    // Token tile matched to small N so no MFMA column work is wasted.  For
+    // larger N, 128x128 tiles of four waves: eight-wave tiles (128x128 and
+    // 256x128) and three or four stages measured within 5% of it on the
+    // 0.6B-class layer.
     if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     return run_gemm<128, 128, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
