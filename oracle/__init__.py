@@ -57,6 +57,14 @@ def lib() -> ctypes.CDLL:
         L.orc_unpack_i2s.restype = _i64
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_absmean_alpha_f32.argtypes = [_p, _i64]
+        L.orc_absmean_alpha_f32.restype = ctypes.c_float
+        L.orc_absmean_alpha_bf16.argtypes = [_p, _i64]
+        L.orc_absmean_alpha_bf16.restype = ctypes.c_float
+        L.orc_absmean_ternary_f32.argtypes = [_p, _i64, ctypes.c_float, _p]
+        L.orc_absmean_ternary_bf16.argtypes = [_p, _i64, ctypes.c_float, _p]
+        L.orc_sign_ternary_f32.argtypes = [_p, _i64, _p, _p]
+        L.orc_sign_ternary_f32.restype = _i64
         L.orc_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.orc_quant_act_f32.restype = None
         L.orc_quant_act_bf16.argtypes = [_p, _i64, _i64, _p, _p, _p]
@@ -204,3 +212,46 @@ def linear_i2s(packed: np.ndarray, K: int, q: np.ndarray, s: np.ndarray,
     if want_y:
         y = np.ascontiguousarray(y[:, r0:r0 + nr])
     return D, y
+
+
+def absmean_alpha(w: np.ndarray) -> float:
+    """AbsMean scale of a whole tensor [P1 §6-2; P4 "Ternary Weight
+    Quantisation (AbsMean)"]: fp32 (float32 array) or bf16 bits (uint16)."""
+    w = np.ascontiguousarray(w)
+    if w.dtype == np.uint16:
+        return float(np.float32(lib().orc_absmean_alpha_bf16(_ptr(w), w.size)))
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    return float(np.float32(lib().orc_absmean_alpha_f32(_ptr(w), w.size)))
+
+
+def absmean_ternary(w: np.ndarray, alpha: float) -> np.ndarray:
+    """q = clip(round-half-even(w / alpha), -1, 1) with one fp32 division
+    [P1 §6-2; P4]; same shape as w, int8."""
+    w = np.ascontiguousarray(w)
+    q = np.empty(w.shape, dtype=np.int8)
+    if w.dtype == np.uint16:
+        lib().orc_absmean_ternary_bf16(_ptr(w), w.size, np.float32(alpha), _ptr(q))
+    else:
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        lib().orc_absmean_ternary_f32(_ptr(w), w.size, np.float32(alpha), _ptr(q))
+    return q
+
+
+def absmean_i2s(w: np.ndarray) -> tuple[np.ndarray, float, np.ndarray]:
+    """AbsMean ternarise a [M][K] weight tensor and pack it to I2_S:
+    returns (packed, alpha, q)."""
+    alpha = absmean_alpha(w)
+    q = absmean_ternary(w, alpha)
+    packed, bad = pack_i2s(q)
+    assert bad == 0
+    return packed, alpha, q
+
+
+def sign_ternary(w: np.ndarray) -> tuple[np.ndarray, float, int]:
+    """Sign/threshold ternary of float weights [P1 §4-2]: (q, max|w|, number
+    of non-finite weights)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    q = np.empty(w.shape, dtype=np.int8)
+    wmax = ctypes.c_float(0.0)
+    bad = lib().orc_sign_ternary_f32(_ptr(w), w.size, _ptr(q), ctypes.byref(wmax))
+    return q, float(np.float32(wmax.value)), int(bad)

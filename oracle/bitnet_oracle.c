@@ -260,3 +260,68 @@ int64_t orc_linear_i2s(const uint8_t *packed, int64_t M, int64_t K,
     }
     return bad;
 }
+
+/* ---- AbsMean ternariser and sign/threshold ternary (weight conversion) ---- */
+
+static float absmean_from_sum(double sum, int64_t n)
+{
+    /* [P1 §6-2]: abs_mean = max(mean(abs(w)), 1e-5); [P4]: alpha_W = mean|W| */
+    float a = (float)(sum / (double)n);
+    return a > 1e-5f ? a : 1e-5f;
+}
+
+float orc_absmean_alpha_f32(const float *w, int64_t n)
+{
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; i++) sum += fabs((double)w[i]);
+    return absmean_from_sum(sum, n);
+}
+
+float orc_absmean_alpha_bf16(const uint16_t *w, int64_t n)
+{
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; i++) sum += fabs((double)orc_bf16_to_f32(w[i]));
+    return absmean_from_sum(sum, n);
+}
+
+static int8_t ternary_of(float v, float alpha)
+{
+    /* [P1 §6-2; P4]: q = clip(round(w / alpha), -1, 1); the division is one
+     * fp32 operation and round is half-to-even (rintf, default mode). */
+    float t = v / alpha;
+    float r = rintf(t);
+    if (r > 1.0f) r = 1.0f;
+    if (r < -1.0f) r = -1.0f;
+    return (int8_t)r;
+}
+
+void orc_absmean_ternary_f32(const float *w, int64_t n, float alpha, int8_t *q)
+{
+    for (int64_t i = 0; i < n; i++) q[i] = ternary_of(w[i], alpha);
+}
+
+void orc_absmean_ternary_bf16(const uint16_t *w, int64_t n, float alpha, int8_t *q)
+{
+    for (int64_t i = 0; i < n; i++) q[i] = ternary_of(orc_bf16_to_f32(w[i]), alpha);
+}
+
+int64_t orc_sign_ternary_f32(const float *w, int64_t n, int8_t *q, float *wmax)
+{
+    /* [P1 §4-2]: near-zero (fabs < 1e-6) -> code 1, positive -> code 2,
+     * negative -> code 0; here as the ternary value (code - 1). */
+    int64_t bad = 0;
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        float v = w[i];
+        if (!isfinite(v)) {
+            bad++;
+            q[i] = 0;
+            continue;
+        }
+        if (fabs((double)v) < 1e-6) q[i] = 0;
+        else q[i] = v > 0.0f ? 1 : -1;
+        if (fabsf(v) > m) m = fabsf(v);
+    }
+    if (wmax) *wmax = m;
+    return bad;
+}

@@ -87,6 +87,25 @@ int64_t orc_linear_i2s(const uint8_t *packed, int64_t M, int64_t K,
                        int64_t row0, int64_t nrows,
                        int64_t *D, double *y, int nthreads);
 
+/* AbsMean ternarisation of full-precision weights [P1 §6-2; P4 "Ternary
+ * Weight Quantisation (AbsMean)"], over all n weights of a tensor:
+ *   alpha = max(mean |w|, 1e-5): the sum of |w| in binary64, divided by n in
+ *           binary64, rounded once to fp32, then the 1e-5 floor (fp32);
+ *   q     = clip(round-half-even(w / alpha), -1, 1), w / alpha one fp32
+ *           division.
+ * Returns alpha; orc_absmean_ternary writes q.  Non-finite weights make alpha
+ * non-finite (the caller treats that as an error). */
+float orc_absmean_alpha_f32(const float *w, int64_t n);
+float orc_absmean_alpha_bf16(const uint16_t *w, int64_t n);
+void orc_absmean_ternary_f32(const float *w, int64_t n, float alpha, int8_t *q);
+void orc_absmean_ternary_bf16(const uint16_t *w, int64_t n, float alpha, int8_t *q);
+
+/* Sign/threshold ternary of float weights, as the packer of [P1 §4-2] reads
+ * them: |v| < 1e-6 (compared in binary64, the constant as written) -> 0,
+ * v > 0 -> +1, v < 0 -> -1.  *wmax (if not NULL) gets max |v|.  Returns the
+ * number of non-finite weights (their q is left 0). */
+int64_t orc_sign_ternary_f32(const float *w, int64_t n, int8_t *q, float *wmax);
+
 #ifdef __cplusplus
 }
 #endif

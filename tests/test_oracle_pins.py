@@ -376,3 +376,129 @@ def test_stored_regression_values(orc):
     rows = kv["rows"]
     assert [int(D[0, r]) for r in rows] == kv["dot"]
     assert os.path.exists(path)
+
+
+# ------------------------------------------------------- AbsMean ternariser
+def _float_fixture(name):
+    kv = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = [float(t) for t in v.split()]
+    return kv
+
+
+def test_absmean_worked_example(orc):
+    """[P1 §6-2]: mean |w| = 0.4 and w / 0.4 = +-0.5, +-1.5 -- exact ties in
+    fp32, so q is decided by the rounding rule (reading: half to even)."""
+    kv = _float_fixture("p1_absmean_example.txt")
+    w = np.array(kv["w"], dtype=np.float32)
+    alpha = orc.absmean_alpha(w)
+    assert np.float32(alpha) == np.float32(kv["mean_abs"][0])
+    ratio = w / np.float32(alpha)                 # IEEE fp32 division
+    np.testing.assert_array_equal(ratio, np.array(kv["ratio"], dtype=np.float32))
+    q = orc.absmean_ternary(w, alpha)
+    np.testing.assert_array_equal(q, np.clip(np.rint(ratio), -1, 1).astype(np.int8))
+    np.testing.assert_array_equal(q, [-1, 0, 0, 1])   # half away from zero: [-1,-1,1,1]
+
+
+def test_absmean_floor_and_constant_tensors(orc):
+    z = np.zeros((4, 128), np.float32)
+    assert orc.absmean_alpha(z) == np.float32(1e-5)
+    assert not orc.absmean_ternary(z, orc.absmean_alpha(z)).any()
+    tiny = np.full((2, 128), 1e-7, np.float32)      # mean below the floor
+    a = orc.absmean_alpha(tiny)
+    assert a == np.float32(1e-5)
+    assert not orc.absmean_ternary(tiny, a).any()
+    c = np.full((8, 128), -0.25, np.float32)
+    a = orc.absmean_alpha(c)
+    assert a == np.float32(0.25)
+    assert (orc.absmean_ternary(c, a) == -1).all()
+
+
+def test_absmean_of_scaled_ternary_is_identity(orc):
+    """W = c*T: mean |W| = c * (nonzero fraction) <= c, so W / alpha rounds
+    to T for every element."""
+    rng = np.random.default_rng(3)
+    T = synth.ternary(rng, 16, 256)
+    frac = np.count_nonzero(T) / T.size
+    for c in (0.01, 0.37, 3.0):
+        W = T.astype(np.float32) * np.float32(c)
+        a = orc.absmean_alpha(W)
+        assert abs(a - c * frac) <= 1e-6 * c
+        np.testing.assert_array_equal(orc.absmean_ternary(W, a), T)
+
+
+def test_absmean_symmetry_and_power_of_two_scaling(orc):
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((32, 384)) * 0.02).astype(np.float32)
+    a = orc.absmean_alpha(W)
+    q = orc.absmean_ternary(W, a)
+    assert orc.absmean_alpha(-W) == a
+    np.testing.assert_array_equal(orc.absmean_ternary(-W, a), -q)
+    for k in (-3, 5):
+        s = np.float32(2.0 ** k)
+        assert orc.absmean_alpha(W * s) == np.float32(a) * s
+        np.testing.assert_array_equal(orc.absmean_ternary(W * s, orc.absmean_alpha(W * s)), q)
+
+
+def test_absmean_half_normal_statistics(orc):
+    """For N(0, sigma^2) weights mean |w| -> sigma*sqrt(2/pi), and q = 0 exactly
+    when |z| < 0.5*sqrt(2/pi), which has probability erf(0.5/sqrt(pi))."""
+    import math
+    rng = np.random.default_rng(5)
+    sigma = 0.02
+    W = (rng.standard_normal((512, 1024)) * sigma).astype(np.float32)
+    a = orc.absmean_alpha(W)
+    assert abs(a / (sigma * math.sqrt(2 / math.pi)) - 1) < 3e-3
+    zero = np.mean(orc.absmean_ternary(W, a) == 0)
+    assert abs(zero - math.erf(0.5 / math.sqrt(math.pi))) < 3e-3
+
+
+def test_absmean_matches_numpy_on_random_tensors(orc):
+    rng = np.random.default_rng(6)
+    for shape in ((3, 128), (17, 640), (64, 1024)):
+        W = (rng.standard_normal(shape) * 0.05).astype(np.float32)
+        a_ref = np.float32(np.abs(W.astype(np.float64)).sum() / W.size)
+        a = orc.absmean_alpha(W)
+        assert a == max(a_ref, np.float32(1e-5))
+        q_ref = np.clip(np.rint(W / np.float32(a)), -1, 1).astype(np.int8)
+        np.testing.assert_array_equal(orc.absmean_ternary(W, a), q_ref)
+
+
+def test_absmean_bf16_is_f32_of_widened_bits(orc):
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((16, 256)) * 0.03).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(W)
+    wide = orc.bf16_to_f32(bits)
+    assert orc.absmean_alpha(bits) == orc.absmean_alpha(wide)
+    np.testing.assert_array_equal(orc.absmean_ternary(bits, orc.absmean_alpha(bits)),
+                                  orc.absmean_ternary(wide, orc.absmean_alpha(wide)))
+
+
+# ------------------------------------------- sign/threshold float packer
+def test_sign_ternary_threshold_edges(orc):
+    """[P1 §4-2]: |v| < 1e-6 is zero, positive -> +1, negative -> -1; the
+    comparison is against the binary64 constant, so fp32(1e-6), which lies
+    just below it, still counts as zero."""
+    one_e6 = np.float32(1e-6)
+    above = np.nextafter(one_e6, np.float32(1))
+    v = np.array([0.0, -0.0, 5e-7, -5e-7, one_e6, -one_e6, above, -above, 2.0, -3.0],
+                 dtype=np.float32)
+    q, wmax, bad = orc.sign_ternary(v)
+    np.testing.assert_array_equal(q, [0, 0, 0, 0, 0, 0, 1, -1, 1, -1])
+    assert wmax == 3.0 and bad == 0
+    q, wmax, bad = orc.sign_ternary(np.array([1.0, np.nan, -np.inf, 0.5], np.float32))
+    assert bad == 2 and wmax == 1.0
+    np.testing.assert_array_equal(q, [1, 0, 0, 1])
+
+
+def test_sign_ternary_of_scaled_ternary_round_trips(orc):
+    rng = np.random.default_rng(8)
+    T = synth.ternary(rng, 8, 384)
+    W = T.astype(np.float32) * np.float32(0.0731)
+    q, wmax, bad = orc.sign_ternary(W)
+    np.testing.assert_array_equal(q, T)
+    assert bad == 0 and wmax == np.float32(0.0731)
