@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the secondary per-row measurements")
-    ap.add_argument("--only", choices=("pack", "quant", "decode", "large", "prefill"),
+    ap.add_argument("--only", choices=("pack", "convert", "quant", "decode", "large", "prefill"),
                     help="run only this group of secondary rows and print them (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
@@ -223,8 +223,8 @@ def secondary_rows(bn, synth, torch, stack, only=None):
     stack where the shapes match (so they stream from HBM), else are drawn
     fresh on the device.  ``only`` picks one group of rows."""
     rows = {}
-    parts = {"pack": row_pack, "quant": row_quant, "decode": row_decode,
-             "large": row_large, "prefill": row_prefill}
+    parts = {"pack": row_pack, "convert": row_convert, "quant": row_quant,
+             "decode": row_decode, "large": row_large, "prefill": row_prefill}
     for name, fn in parts.items():
         if only is None or only == name:
             rows.update(fn(bn, synth, torch, stack))
@@ -247,6 +247,26 @@ def row_pack(bn, synth, torch, stack):
                     "GB/s": round((M * K + M * K // 4) / t / 1e9, 1),
                     "note": "includes the stream sync that reads the bad-value count"}
     del W, out
+    return rows
+
+
+def row_convert(bn, synth, torch, stack):
+    """NEXT f2: one-time conversion of a 6912x2560 bf16 weight (2B-class gate)
+    with the AbsMean ternariser, and of fp32 already-ternary weights with the
+    sign/threshold packer.  Both synchronise (they return the scale on the
+    host); the AbsMean call reads the weights twice (sum, then pack)."""
+    rows = {}
+    M, K = synth.SHAPES["b2"]["gate"]
+    W = synth.tokens_bf16_torch(M, K, 21) * 0.02          # N(0, 0.02^2) bf16 weights
+    t = _events_time(torch, lambda: bn.absmean_pack(W), 10)
+    rows["absmean_pack"] = {"shape": f"{M}x{K} bf16", "us": round(t * 1e6, 2),
+                            "GB/s": round((M * K * 2 + M * K // 4) / t / 1e9, 1),
+                            "note": "two passes over the weights; includes the stream sync"}
+    Wf = synth.ternary_torch(M, K, 22).float() * 0.05
+    t = _events_time(torch, lambda: bn.pack_f32(Wf), 10)
+    rows["pack_f32"] = {"shape": f"{M}x{K} fp32", "us": round(t * 1e6, 2),
+                        "GB/s": round((M * K * 4 + M * K // 4) / t / 1e9, 1),
+                        "note": "includes the stream sync"}
     return rows
 
 

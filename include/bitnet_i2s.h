@@ -183,6 +183,42 @@ int bitnet_gemm_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t 
                              const int8_t *xq, const float *x_scale,
                              const int32_t *x_sum, int64_t N, void *stream);
 
+/*
+ * bitnet_absmean_i2s -- one-time conversion of full-precision weights to I2_S
+ * with the AbsMean ternariser.  [P1 §6-2; P4 "Ternary Weight Quantisation
+ * (AbsMean)"; layout P1 §1-1, §4-2]
+ *
+ *   w       device [M][K] fp32 or bf16 (dtype BITNET_F32 / BITNET_BF16),
+ *           16-byte aligned; M >= 1.
+ *   packed  device [M][K/4] I2_S output, 16-byte aligned.
+ *   alpha   HOST pointer; receives the per-tensor scale
+ *           alpha = max(mean |w| over all M*K weights, 1e-5), the sum of |w|
+ *           taken in binary64 in a fixed order and the mean rounded once to
+ *           fp32.  Use it as w_scale of the matmul calls.
+ *
+ * Each weight becomes q = clip(round-half-even(w / alpha), -1, 1), w / alpha
+ * one fp32 division, stored as code q + 1.  Synchronises `stream`
+ * (the scale is returned on the host); calls are serialised inside the
+ * library.  Non-finite weights -> BITNET_E_VALUE (packed then unspecified).
+ */
+int bitnet_absmean_i2s(const void *w, int dtype, int64_t M, int64_t K,
+                       uint8_t *packed, float *alpha, void *stream);
+
+/*
+ * bitnet_pack_i2s_f32 -- pack float weights that are already ternary in value
+ * (e.g. q * scale) by sign: |v| < 1e-6 (compared in binary64) -> code 1,
+ * v > 0 -> code 2, v < 0 -> code 0.  [P1 §4-2 (the float packer), §1-1]
+ *
+ *   w       device [M][K] fp32, 16-byte aligned.
+ *   packed  device [M][K/4] I2_S output, 16-byte aligned.
+ *   w_max   HOST pointer or NULL; receives max |w| (0 for M == 0).
+ *
+ * Synchronises `stream`; M == 0 is a no-op.  Non-finite weights ->
+ * BITNET_E_VALUE (packed then unspecified).
+ */
+int bitnet_pack_i2s_f32(const float *w, int64_t M, int64_t K, uint8_t *packed,
+                        float *w_max, void *stream);
+
 /* Thread-local description of the last non-OK status on this thread
  * (empty string if none).  The pointer stays valid until the next call on
  * the same thread. */

@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
     L.bitnet_gemm_i2s_i8_group.argtypes = [ctypes.POINTER(I2SMatrix), ctypes.c_int, i64, p, p, p,
                                            i64, p]
     L.bitnet_gemm_i2s_i8_group.restype = ctypes.c_int
+    L.bitnet_absmean_i2s.argtypes = [p, ctypes.c_int, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
+    L.bitnet_absmean_i2s.restype = ctypes.c_int
+    L.bitnet_pack_i2s_f32.argtypes = [p, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
+    L.bitnet_pack_i2s_f32.restype = ctypes.c_int
     for fn in ("bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
                "bitnet_gemm_i2s_i8", "bitnet_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
@@ -107,6 +111,39 @@ def pack(w):
     out = torch.empty((M, K // 4 if K % 4 == 0 else 0), dtype=torch.uint8, device=w.device)
     _check(load().bitnet_pack_i2s(_ptr(w), M, K, _ptr(out), _stream(w)))
     return out
+
+
+def absmean_pack(w, out=None):
+    """fp32 or bf16 weights W[M][K] (cuda) -> (uint8 I2_S packed[M][K/4], AbsMean
+    scale alpha as a Python float)."""
+    import torch
+    if w.dim() != 2:
+        raise TypeError("w must be 2-D [M][K]")
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(w.dtype)
+    if dt is None:
+        raise TypeError("w must be float32 or bfloat16")
+    M, K = w.shape
+    packed = out if out is not None else torch.empty((M, K // 4 if K % 4 == 0 else 0),
+                                                     dtype=torch.uint8, device=w.device)
+    alpha = ctypes.c_float(0.0)
+    _check(load().bitnet_absmean_i2s(_ptr(w), dt, M, K, _ptr(packed), ctypes.byref(alpha),
+                                     _stream(w)))
+    return packed, alpha.value
+
+
+def pack_f32(w, out=None):
+    """fp32 weights already ternary in value, W[M][K] (cuda) -> (packed I2_S by
+    sign with the 1e-6 zero threshold, max|w| as a Python float)."""
+    import torch
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise TypeError("w must be a 2-D float32 tensor")
+    M, K = w.shape
+    packed = out if out is not None else torch.empty((M, K // 4 if K % 4 == 0 else 0),
+                                                     dtype=torch.uint8, device=w.device)
+    wmax = ctypes.c_float(0.0)
+    _check(load().bitnet_pack_i2s_f32(_ptr(w), M, K, _ptr(packed), ctypes.byref(wmax),
+                                      _stream(w)))
+    return packed, wmax.value
 
 
 def quant_act(x, out=None):

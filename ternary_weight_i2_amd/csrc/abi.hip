@@ -68,6 +68,35 @@ int pack_counter(int dev, unsigned **out) {
     return BITNET_OK;
 }
 
+// Scratch of the one-time weight conversion calls (AbsMean partial sums, the
+// scale, the non-finite count and max|w|).  Like the pack counter: one copy
+// per device, its address looked up once per device, and the calls that use
+// it serialised by g_pack_mu and synchronised before they return.
+struct ConvScratch {
+    double partial[bitnet::kConvPartials];
+    float alpha;
+    unsigned bad;
+    float wmax;
+};
+__device__ ConvScratch g_conv;
+void *g_conv_addr[kMaxDevices];
+
+int conv_scratch(const char *fn, ConvScratch **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BITNET_E_HIP, "%s: device index %d unsupported", fn, dev);
+    if (!g_conv_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_conv));
+        if (e != hipSuccess) return hip_fail(fn, e);
+        g_conv_addr[dev] = p;
+    }
+    *out = static_cast<ConvScratch *>(g_conv_addr[dev]);
+    return BITNET_OK;
+}
+
 int check_matmul(const char *fn, const uint8_t *packed, int64_t M, int64_t K,
                  const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
                  int64_t max_n, const int32_t *dot, const float *y) {
@@ -125,6 +154,64 @@ BITNET_API int bitnet_pack_i2s(const int8_t *w, int64_t M, int64_t K, uint8_t *p
         return hip_fail("bitnet_pack_i2s: synchronize", e);
     if (nbad)
         return fail(BITNET_E_VALUE, "%s: %u weight(s) outside {-1,0,+1}", fn, nbad);
+    return ok();
+}
+
+BITNET_API int bitnet_absmean_i2s(const void *w, int dtype, int64_t M, int64_t K,
+                                  uint8_t *packed, float *alpha, void *stream) {
+    const char *fn = "bitnet_absmean_i2s";
+    if (dtype != BITNET_F32 && dtype != BITNET_BF16)
+        return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (M < 1) return fail(BITNET_E_SHAPE, "%s: M=%lld, need at least one row", fn, (long long)M);
+    if (int s = check_k(fn, K)) return s;
+    if (!w || !packed || !alpha) return fail(BITNET_E_NULL, "%s: w, packed and alpha are required", fn);
+    if (!aligned(w, 16) || !aligned(packed, 16))
+        return fail(BITNET_E_ALIGN, "%s: w and packed must be 16-byte aligned", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    ConvScratch *sc = nullptr;
+    if (int s = conv_scratch(fn, &sc)) return s;
+    hipError_t e = hipMemsetAsync(&sc->bad, 0, sizeof(unsigned), st);
+    const int bf16 = dtype == BITNET_BF16;
+    if (e == hipSuccess) e = bitnet::launch_absmean_alpha(w, bf16, M * K, sc->partial, &sc->alpha, st);
+    if (e == hipSuccess)
+        e = bitnet::launch_ternary_pack(w, bf16, 0, M, K, &sc->alpha, packed, &sc->bad, nullptr,
+                                        nullptr, st);
+    struct { float alpha; unsigned bad; } res{};
+    if (e == hipSuccess) e = hipMemcpyAsync(&res, &sc->alpha, sizeof res, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (res.bad) return fail(BITNET_E_VALUE, "%s: %u non-finite weight(s)", fn, res.bad);
+    *alpha = res.alpha;
+    return ok();
+}
+
+BITNET_API int bitnet_pack_i2s_f32(const float *w, int64_t M, int64_t K, uint8_t *packed,
+                                   float *w_max, void *stream) {
+    const char *fn = "bitnet_pack_i2s_f32";
+    if (M < 0) return fail(BITNET_E_SHAPE, "%s: negative M=%lld", fn, (long long)M);
+    if (int s = check_k(fn, K)) return s;
+    if (M == 0) {
+        if (w_max) *w_max = 0.0f;
+        return ok();
+    }
+    if (!w || !packed) return fail(BITNET_E_NULL, "%s: w and packed are required", fn);
+    if (!aligned(w, 16) || !aligned(packed, 16))
+        return fail(BITNET_E_ALIGN, "%s: w and packed must be 16-byte aligned", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_pack_mu);
+    ConvScratch *sc = nullptr;
+    if (int s = conv_scratch(fn, &sc)) return s;
+    hipError_t e = hipMemsetAsync(&sc->bad, 0, sizeof(unsigned), st);
+    if (e == hipSuccess)
+        e = bitnet::launch_ternary_pack(w, 0, 1, M, K, nullptr, packed, &sc->bad, sc->partial,
+                                        &sc->wmax, st);
+    struct { unsigned bad; float wmax; } res{};
+    if (e == hipSuccess) e = hipMemcpyAsync(&res, &sc->bad, sizeof res, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (res.bad) return fail(BITNET_E_VALUE, "%s: %u non-finite weight(s)", fn, res.bad);
+    if (w_max) *w_max = res.wmax;
     return ok();
 }
 

@@ -174,4 +174,12 @@ struct GemmArgs {
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st);
 
+// One-time weight conversion (AbsMean ternariser, sign/threshold packer).
+constexpr int kConvPartials = 1024;   // partial sums of the AbsMean reduction
+hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, double *partial,
+                                float *alpha, hipStream_t st);
+hipError_t launch_ternary_pack(const void *w, int bf16, int mode, int64_t M, int64_t K,
+                               const float *alpha, uint8_t *packed, unsigned *bad,
+                               double *part, float *wmax, hipStream_t st);
+
 }  // namespace bitnet

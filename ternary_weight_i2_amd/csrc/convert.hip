@@ -1,0 +1,201 @@
+// convert.hip -- one-time weight conversion to I2_S: the AbsMean ternariser
+// and the sign/threshold float packer.
+//
+// Pages: [P1] "BitNet 딥다이브" §6-2 (AbsMean: scale = max(mean|w|, 1e-5),
+// q = round(w / scale) limited to -1..1, the scale stored for dequantisation),
+// §4-2 (the float packer: near-zero weights, |v| < 1e-6, take code 1,
+// positive ones code 2, negative ones code 0), §1-1 (code table); [P4]
+// "bitnet.rs", "Mathematical Foundation" (AbsMean formula).
+//
+// AbsMean in two deterministic passes over the tensor: a fixed grid of
+// workgroups each sums |w| of a fixed, strided share in binary64
+// (partial[]), then one workgroup adds the partials in a fixed order and
+// rounds the mean once to fp32.  The same input therefore always gives the
+// same alpha.  The pack pass then reads alpha from device memory, so the
+// three launches need no host round trip.
+#include "common.h"
+
+namespace bitnet {
+
+constexpr int kConvThreads = 256;
+
+// 4 consecutive weights, widened to fp32 (16 bytes of fp32 or 8 of bf16)
+template <int BF16>
+__device__ __forceinline__ void load4(const void *w, int64_t g, float *v) {
+    if constexpr (BF16) {
+        const uint2 u = reinterpret_cast<const uint2 *>(w)[g];
+        v[0] = __uint_as_float(u.x << 16);
+        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(u.y << 16);
+        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+        const float4 f = reinterpret_cast<const float4 *>(w)[g];
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Pass 1: partial[b] = sum of |w| over groups of 4 weights g = b*256 + t,
+// g += gridDim*256 (binary64; order fixed by the grid).
+template <int BF16>
+__global__ __launch_bounds__(kConvThreads) void absmean_partial_kernel(
+    const void *__restrict__ w, int64_t n4, double *__restrict__ partial) {
+    __shared__ double red[kConvThreads / 64];
+    double acc = 0.0;
+    for (int64_t g = (int64_t)blockIdx.x * kConvThreads + threadIdx.x; g < n4;
+         g += (int64_t)gridDim.x * kConvThreads) {
+        float v[4];
+        load4<BF16>(w, g, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += fabs((double)v[e]);
+    }
+    acc = wave_sum_f64(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < kConvThreads / 64; ++i) s += red[i];
+        partial[blockIdx.x] = s;
+    }
+}
+
+// Pass 2 (one workgroup): alpha = max(fp32(sum / n), 1e-5).
+__global__ __launch_bounds__(1024) void absmean_final_kernel(
+    const double *__restrict__ partial, int nparts, int64_t n, float *__restrict__ alpha) {
+    __shared__ double red[16];
+    double v = (int)threadIdx.x < nparts ? partial[threadIdx.x] : 0.0;
+    v = wave_sum_f64(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += red[i];
+        const float a = (float)(s / (double)n);
+        *alpha = a > 1e-5f ? a : 1e-5f;
+    }
+}
+
+// Pass 3: one thread per packed dword (bytes g0..g0+3 of a 32-byte block =
+// block positions g0+e+32*i), as the int8 packer.  MODE 0: AbsMean,
+// q = clip(rint(w / alpha), -1, 1) with one fp32 division.  MODE 1: sign with
+// the |v| < 1e-6 zero threshold (compared in binary64, as the constant is
+// written), and each workgroup's max|v| into part[] (the grid is then at
+// most kConvPartials workgroups; max_final_kernel reduces them).
+// Non-finite weights are counted in *bad (code 1).
+template <int BF16, int MODE>
+__global__ __launch_bounds__(kConvThreads) void ternary_pack_kernel(
+    const void *__restrict__ w, int64_t M, int64_t K, const float *__restrict__ alpha,
+    uint8_t *__restrict__ packed, unsigned *__restrict__ bad, double *__restrict__ part) {
+    const int64_t dw_per_row = K / 16;
+    const int64_t total = M * dw_per_row;
+    const float a = MODE == 0 ? *alpha : 1.0f;
+    unsigned nbad = 0;
+    float vmax = 0.0f;
+    for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
+         d += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = d / dw_per_row;
+        const int64_t r = d - m * dw_per_row;
+        const int64_t blk = r >> 3;          // 8 dwords per block
+        const int g0 = (int)(r & 7) * 4;     // first block byte of this dword
+        const int64_t base = m * K + blk * kBlock + g0;   // element index, multiple of 4
+        uint32_t out = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v[4];
+            load4<BF16>(w, (base + 32 * i) >> 2, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int code = 1;
+                if (!__builtin_isfinite(v[e])) {
+                    ++nbad;
+                } else if constexpr (MODE == 0) {
+                    const float q = fminf(fmaxf(__builtin_rintf(v[e] / a), -1.0f), 1.0f);
+                    code = (int)q + 1;
+                } else {
+                    if (fabs((double)v[e]) >= 1e-6) code = v[e] > 0.0f ? 2 : 0;
+                    vmax = fmaxf(vmax, fabsf(v[e]));
+                }
+                out |= (uint32_t)code << (8 * e + 6 - 2 * i);
+            }
+        }
+        *reinterpret_cast<uint32_t *>(packed + m * (K / 4) + blk * kBlockBytes + g0) = out;
+    }
+    if (nbad) atomicAdd(bad, nbad);
+    if constexpr (MODE == 1) {
+        __shared__ float red[kConvThreads / 64];
+        vmax = wave_max_f32(vmax);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = vmax;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float m = red[0];
+#pragma unroll
+            for (int i = 1; i < kConvThreads / 64; ++i) m = fmaxf(m, red[i]);
+            part[blockIdx.x] = (double)m;
+        }
+    }
+}
+
+// max over nparts workgroup maxima (one workgroup) -> *wmax
+__global__ __launch_bounds__(1024) void max_final_kernel(const double *__restrict__ part,
+                                                         int nparts, float *__restrict__ wmax) {
+    __shared__ float red[16];
+    float v = (int)threadIdx.x < nparts ? (float)part[threadIdx.x] : 0.0f;
+    v = wave_max_f32(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = red[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i]);
+        *wmax = m;
+    }
+}
+
+hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, double *partial,
+                                float *alpha, hipStream_t st) {
+    const int64_t n4 = n / 4;
+    int64_t parts = (n4 + kConvThreads * 8 - 1) / (kConvThreads * 8);   // >= 8 groups per thread
+    if (parts > kConvPartials) parts = kConvPartials;
+    if (parts < 1) parts = 1;
+    if (bf16)
+        hipLaunchKernelGGL(absmean_partial_kernel<1>, dim3((unsigned)parts), dim3(kConvThreads), 0, st,
+                           w, n4, partial);
+    else
+        hipLaunchKernelGGL(absmean_partial_kernel<0>, dim3((unsigned)parts), dim3(kConvThreads), 0, st,
+                           w, n4, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(1024), 0, st, partial, (int)parts, n,
+                       alpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_ternary_pack(const void *w, int bf16, int mode, int64_t M, int64_t K,
+                               const float *alpha, uint8_t *packed, unsigned *bad,
+                               double *part, float *wmax, hipStream_t st) {
+    const int64_t total = M * (K / 16);
+    int64_t blocks = (total + kConvThreads - 1) / kConvThreads;
+    const int64_t cap = mode == 0 ? 65536 : kConvPartials;
+    if (blocks > cap) blocks = cap;
+    const dim3 g((unsigned)blocks), b(kConvThreads);
+    if (mode == 0) {
+        if (bf16) hipLaunchKernelGGL((ternary_pack_kernel<1, 0>), g, b, 0, st, w, M, K, alpha, packed, bad, part);
+        else hipLaunchKernelGGL((ternary_pack_kernel<0, 0>), g, b, 0, st, w, M, K, alpha, packed, bad, part);
+        return hipGetLastError();
+    }
+    if (bf16) hipLaunchKernelGGL((ternary_pack_kernel<1, 1>), g, b, 0, st, w, M, K, alpha, packed, bad, part);
+    else hipLaunchKernelGGL((ternary_pack_kernel<0, 1>), g, b, 0, st, w, M, K, alpha, packed, bad, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(1024), 0, st, part, (int)blocks, wmax);
+    return hipGetLastError();
+}
+
+}  // namespace bitnet

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
     fns = set(declared_functions())
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
             "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_linear_i2s",
-            "bitnet_last_error", "bitnet_abi_version"} <= fns
+            "bitnet_absmean_i2s", "bitnet_pack_i2s_f32", "bitnet_last_error",
+            "bitnet_abi_version"} <= fns
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -185,6 +186,32 @@ def test_gemm_group_validation(L):
     # no-ops: N == 0, or every matrix empty
     assert f(g1, 1, 256, None, None, None, 0, None) == OK
     assert f(mats(I2SMatrix(None, 0, 0.1, None, None)), 1, 256, None, None, None, 4, None) == OK
+    assert _err(L) == ""
+
+
+def test_conversion_validation(L):
+    import ctypes
+    a = ctypes.c_float(0.0)
+    f = L.bitnet_absmean_i2s
+    assert f(FAKE, 3, 4, 128, FAKE, ctypes.byref(a), None) == E_DTYPE
+    assert f(FAKE, 0, 0, 128, FAKE, ctypes.byref(a), None) == E_SHAPE   # no rows: no scale
+    assert "at least one row" in _err(L)
+    assert f(FAKE, 0, 4, 100, FAKE, ctypes.byref(a), None) == E_SHAPE
+    assert f(FAKE, 1, 4, 32768 + 128, FAKE, ctypes.byref(a), None) == E_SHAPE
+    assert f(None, 0, 4, 128, FAKE, ctypes.byref(a), None) == E_NULL
+    assert f(FAKE, 0, 4, 128, None, ctypes.byref(a), None) == E_NULL
+    assert f(FAKE, 0, 4, 128, FAKE, None, None) == E_NULL
+    assert f(FAKE + 8, 1, 4, 128, FAKE, ctypes.byref(a), None) == E_ALIGN
+    assert f(FAKE, 0, 4, 128, MIS, ctypes.byref(a), None) == E_ALIGN
+    g = L.bitnet_pack_i2s_f32
+    assert g(FAKE, -1, 128, FAKE, None, None) == E_SHAPE
+    assert g(FAKE, 4, 96, FAKE, None, None) == E_SHAPE
+    assert g(None, 4, 128, FAKE, None, None) == E_NULL
+    assert g(FAKE, 4, 128, None, None, None) == E_NULL
+    assert g(FAKE + 4, 4, 128, FAKE, None, None) == E_ALIGN
+    assert g(FAKE, 4, 128, MIS, None, None) == E_ALIGN
+    a.value = 7.0
+    assert g(None, 0, 128, None, ctypes.byref(a), None) == OK and a.value == 0.0
     assert _err(L) == ""
 
 

@@ -416,3 +416,107 @@ def test_linear_e06_prefill_layer(bn):
         K = synth.SHAPES["e06"][projs[0]][1]
         run_linear(bn, Ms, K, 256, "bf16", seed=K + len(projs),
                    rows=[(0, 24), (min(Ms) - 24, 24)])
+
+
+# ------------------------------------------------ one-time weight conversion
+def check_absmean(bn, W, bits=None):
+    """AbsMean ternariser on the GPU vs the oracle.  alpha: the same fp32 value
+    (the binary64 sums may differ in their last bits only, so 1 ulp is allowed);
+    codes: bit for bit with the oracle's ternary step taken at the GPU's alpha
+    (the decision in the same precision), and with the oracle's own result
+    whenever the two alphas agree."""
+    if bits is not None:
+        wg = to_bf16_tensor(bits)
+        host = bits
+    else:
+        wg = dev(W)
+        host = W
+    packed, alpha = bn.absmean_pack(wg)
+    torch.cuda.synchronize()
+    a_ref = oracle.absmean_alpha(host)
+    assert abs(np.float32(alpha) - np.float32(a_ref)) <= np.spacing(np.float32(a_ref))
+    q_at_gpu_alpha = oracle.absmean_ternary(host, alpha)
+    P_ref, bad = oracle.pack_i2s(q_at_gpu_alpha)
+    assert bad == 0
+    np.testing.assert_array_equal(packed.cpu().numpy(), P_ref)
+    if np.float32(alpha) == np.float32(a_ref):
+        np.testing.assert_array_equal(packed.cpu().numpy(), oracle.absmean_i2s(host)[0])
+    return packed, alpha
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (7, 384), (257, 640), (2560, 2560), (64, 32768)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_absmean_i2s(bn, M, K, dtype):
+    rng = np.random.default_rng(M + K)
+    W = (rng.standard_normal((M, K)) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        check_absmean(bn, None, bits=synth.f32_to_bf16_bits(W))
+    else:
+        check_absmean(bn, W)
+
+
+def test_absmean_page_example_and_edges(bn):
+    """The page's four weights (repeated to one block) give alpha = 0.4 and
+    q = [-1, 0, 0, 1] under half-to-even; an all-zero tensor takes the floor."""
+    W = np.tile(np.array([-0.6, -0.2, 0.2, 0.6], np.float32), 32).reshape(1, 128)
+    packed, alpha = check_absmean(bn, W)
+    assert np.float32(alpha) == np.float32(0.4)
+    q, _ = oracle.unpack_i2s(packed.cpu().numpy(), 128)
+    np.testing.assert_array_equal(q[0, :4], [-1, 0, 0, 1])
+    packed, alpha = check_absmean(bn, np.zeros((3, 256), np.float32))
+    assert np.float32(alpha) == np.float32(1e-5)
+    assert (packed.cpu().numpy() == 0x55).all()          # every code 1
+    rng = np.random.default_rng(9)
+    T = synth.ternary(rng, 33, 512)
+    packed, alpha = check_absmean(bn, T.astype(np.float32) * np.float32(0.125))
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.pack_i2s(T)[0])
+
+
+def test_absmean_rejects_non_finite(bn):
+    W = np.zeros((2, 128), np.float32)
+    W[1, 5] = np.inf
+    with pytest.raises(bn.BitnetError) as e:
+        bn.absmean_pack(dev(W))
+    assert e.value.status == 5 and "non-finite" in str(e.value)
+
+
+def test_absmean_output_feeds_the_matmul(bn):
+    """AbsMean-packed weights and their alpha through the fused decode linear:
+    the same result as the oracle on the oracle's ternary weights."""
+    rng = np.random.default_rng(10)
+    M, K = 640, 2560
+    W = (rng.standard_normal((M, K)) * 0.02).astype(np.float32)
+    packed, alpha = check_absmean(bn, W)
+    x = synth.tokens_bf16(rng, 1, K)
+    (d, y), = bn.linear(to_bf16_tensor(x), [(packed, alpha)])[0]
+    torch.cuda.synchronize()
+    q, s, qs = oracle.quant_act(x)
+    D, _ = oracle.linear_i2s(packed.cpu().numpy(), K, q, s, alpha, nthreads=8, want_y=False)
+    np.testing.assert_array_equal(d.cpu().numpy(), D)
+    check_y(y.cpu().numpy(), D, alpha, s)
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (9, 384), (2560, 2560)])
+def test_pack_f32_threshold(bn, M, K):
+    rng = np.random.default_rng(M * 3 + K)
+    T = synth.ternary(rng, M, K)
+    W = T.astype(np.float32) * np.float32(0.031)
+    # sprinkle values near the threshold and signed zeros
+    flat = W.reshape(-1)
+    idx = rng.choice(flat.size, size=min(64, flat.size), replace=False)
+    edge = np.array([5e-7, -5e-7, np.float32(1e-6), -np.float32(1e-6),
+                     np.nextafter(np.float32(1e-6), np.float32(1)), -0.0, 2.5, -4.0], np.float32)
+    flat[idx] = edge[np.arange(idx.size) % edge.size]
+    packed, wmax = bn.pack_f32(dev(W))
+    torch.cuda.synchronize()
+    q, wmax_ref, bad = oracle.sign_ternary(W)
+    assert bad == 0 and np.float32(wmax) == np.float32(wmax_ref)
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.pack_i2s(q)[0])
+
+
+def test_pack_f32_rejects_non_finite(bn):
+    W = np.zeros((2, 128), np.float32)
+    W[0, 77] = np.nan
+    with pytest.raises(bn.BitnetError) as e:
+        bn.pack_f32(dev(W))
+    assert e.value.status == 5
