@@ -60,6 +60,7 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
     int64_t total_rows = 0;
     for (int i = 0; i < nmats; ++i) total_rows += mats[i].M;
     const GemvGeometry geo = gemv_geometry(K, total_rows, mode);
+    const int C = (int)(K >> 6);
     const int lpr = geo.lpr, rows_per_wg = geo.rows_per_wg, per = geo.per;
     const int esize = mode == 0 ? 1 : (mode == 1 ? 4 : 2);
     for (int64_t n0 = 0; n0 < N; n0 += per) {
@@ -89,16 +90,17 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
         if (wg == 0) continue;
         hipError_t e;
         const unsigned g = (unsigned)wg;
+        const bool sr = nt == 1 && (C + lpr - 1) / lpr <= 4;   // J <= 4: short-row kernels
         if (nt == 1)
-            e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, g, st)
-              : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, g, st) : launch_gemv_nt<1, 2>(a, lpr, g, st);
+            e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, sr, g, st)
+              : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, sr, g, st) : launch_gemv_nt<1, 2>(a, lpr, sr, g, st);
         else if (nt == 2)
-            e = mode == 0 ? launch_gemv_nt<2, 0>(a, lpr, g, st)
-              : mode == 1 ? launch_gemv_nt<2, 1>(a, lpr, g, st) : launch_gemv_nt<2, 2>(a, lpr, g, st);
+            e = mode == 0 ? launch_gemv_nt<2, 0>(a, lpr, sr, g, st)
+              : mode == 1 ? launch_gemv_nt<2, 1>(a, lpr, sr, g, st) : launch_gemv_nt<2, 2>(a, lpr, sr, g, st);
         else if (nt <= 4)
-            e = mode == 1 ? launch_gemv_nt<4, 1>(a, lpr, g, st) : launch_gemv_nt<4, 2>(a, lpr, g, st);
+            e = mode == 1 ? launch_gemv_nt<4, 1>(a, lpr, sr, g, st) : launch_gemv_nt<4, 2>(a, lpr, sr, g, st);
         else
-            e = mode == 1 ? launch_gemv_nt<8, 1>(a, lpr, g, st) : launch_gemv_nt<8, 2>(a, lpr, g, st);
+            e = mode == 1 ? launch_gemv_nt<8, 1>(a, lpr, sr, g, st) : launch_gemv_nt<8, 2>(a, lpr, sr, g, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -236,13 +236,15 @@ struct TokenPrologue {
 #ifndef BITNET_GEMV_XDIRECT
 #define BITNET_GEMV_XDIRECT 0         // 1: mode 0 reads int8 tokens from global memory
 #endif
-#ifndef BITNET_GEMV_JM
-#define BITNET_GEMV_JM 8              // chunks per lane per row group (upper bound)
-#endif
 
-template <int NT, int LPR, int MODE>
+// JM: chunks per lane per row group (upper bound of J).  JM = 4 is the
+// short-row variant for single-token launches with J <= 4: its chunk loop has
+// no run-time guard (chunks past J carry zeroed weights), so the compiler can
+// issue every chunk's LDS reads at once -- the tail after the weights arrive
+// is a latency chain in these small launches.
+template <int NT, int LPR, int MODE, int JM>
 __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs a) {
-    constexpr int JM = BITNET_GEMV_JM;
+    constexpr bool kAllChunks = JM == 4;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
     int8_t *xl = reinterpret_cast<int8_t *>(lds);
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
             const int c = u + LPR * j;
-            if (j < J) {
+            if (kAllChunks || j < J) {
                 const bool ok = c < C && row_ok;
                 const int pw[4] = {ok ? w[j].x : 0, ok ? w[j].y : 0, ok ? w[j].z : 0,
                                    ok ? w[j].w : 0};
@@ -440,20 +442,32 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
 // One launch of the kernel for NT tokens per pass, token mode MODE and the
 // lane count chosen by the host.  Each (NT, MODE) pair is instantiated in one
 // of the gemv_valu_n*.hip translation units.
-template <int NT, int MODE>
-hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, unsigned grid, hipStream_t st) {
+template <int NT, int MODE, int JM>
+static hipError_t launch_gemv_ntj(const GemvArgs &a, int lpr, unsigned grid, hipStream_t st) {
     const size_t lds = (size_t)a.ntok * (size_t)a.K;
     switch (lpr) {
-        case 8: hipLaunchKernelGGL((gemv_valu_kernel<NT, 8, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((gemv_valu_kernel<NT, 16, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((gemv_valu_kernel<NT, 32, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        default: hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 8: hipLaunchKernelGGL((gemv_valu_kernel<NT, 8, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((gemv_valu_kernel<NT, 16, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((gemv_valu_kernel<NT, 32, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        default: hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
     }
     return hipGetLastError();
 }
 
+// One launch of the kernel for NT tokens per pass, token mode MODE and the
+// lane count chosen by the host (short: J <= 4, taken for NT == 1 only).
+// Each (NT, MODE) pair is instantiated in one of the gemv_valu_n*.hip
+// translation units.
+template <int NT, int MODE>
+hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, bool short_rows, unsigned grid,
+                          hipStream_t st) {
+    if constexpr (NT == 1)
+        if (short_rows) return launch_gemv_ntj<NT, MODE, 4>(a, lpr, grid, st);
+    return launch_gemv_ntj<NT, MODE, 8>(a, lpr, grid, st);
+}
+
 #define BITNET_GEMV_EXTERN(NT, MODE) \
-    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, unsigned, hipStream_t)
+    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, bool, unsigned, hipStream_t)
 // int8 tokens (mode 0) take at most two per pass; the fused modes up to eight
 BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);
 BITNET_GEMV_EXTERN(2, 0); BITNET_GEMV_EXTERN(2, 1); BITNET_GEMV_EXTERN(2, 2);

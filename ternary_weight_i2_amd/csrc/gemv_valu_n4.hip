@@ -3,6 +3,6 @@
 #include "gemv_valu.h"
 
 namespace bitnet {
-template hipError_t launch_gemv_nt<4, 1>(const GemvArgs &, int, unsigned, hipStream_t);
-template hipError_t launch_gemv_nt<4, 2>(const GemvArgs &, int, unsigned, hipStream_t);
+template hipError_t launch_gemv_nt<4, 1>(const GemvArgs &, int, bool, unsigned, hipStream_t);
+template hipError_t launch_gemv_nt<4, 2>(const GemvArgs &, int, bool, unsigned, hipStream_t);
 }  // namespace bitnet
