@@ -31,9 +31,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # HBM bytes per launch of the fused GEMV, from rocprofv3 FETCH_SIZE (x2.0) and
 # WRITE_SIZE (x1.0) scaled by a 256 MiB copy (profiles/gemv_b2_decode_hbm_traffic.md);
 # valid only for the kernel sources with this sha256.
-TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv.hip", "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "1bcd9a555bdeff19c87aa1bccb30f33f23253c48b597d7e714ebb66f1cb986aa",
-           "bytes_per_launch": 4589056}
+TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
+                       "ternary_weight_i2_amd/csrc/common.h"),
+           "sha256": "1c43d5733cf67cf90848d094f05f8b232939b8626edf9f91a6f1e6c42385ac12",
+           "bytes_per_launch": 4578816}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
@@ -316,38 +317,59 @@ def row_decode(bn, synth, torch, stack):
 
 
 def row_large(bn, synth, torch, stack):
+    """a3 at streaming sizes: the large-layer stack (8 layers x 7 projections,
+    1.71 GB packed, streamed from HBM every step) at N = 1 and 16, one fused
+    quantise + GEMV launch per dependency group (q/k/v, o, gate/up, down) on
+    bf16 tokens; at N = 1 also the per-matrix GEMV on int8 tokens."""
     rows = {}
-    # a3 at streaming sizes: large layer (8 layers x 7 projections, 1.71 GB), N = 1 and 16
-    large = []
+    layers = []
     for l in range(8):
-        for p in synth.PROJ_NAMES:
-            M, K = synth.SHAPES["large"][p]
-            W = synth.ternary_torch(M, K, synth.stack_seed("large", l, p, "weights"))
-            large.append((bn.pack(W), synth.weight_scale(synth.rng_for("large", l, p, "scale")), M, K))
-            del W
-    for N in (1, 16):
+        groups = []
+        for _, projs in GROUPS:
+            K = synth.SHAPES["large"][projs[0]][1]
+            mats = []
+            for p in projs:
+                M, Kp = synth.SHAPES["large"][p]
+                W = synth.ternary_torch(M, Kp, synth.stack_seed("large", l, p, "weights"))
+                mats.append((bn.pack(W), synth.weight_scale(synth.rng_for("large", l, p, "scale"))))
+                del W
+            groups.append((K, mats))
+        layers.append(groups)
+    packed = sum(P.numel() for groups in layers for K, mats in groups for P, _ in mats)
+    for N, how in ((1, "linear"), (1, "gemv"), (16, "linear")):
         bufs = []
-        qs = {}
-        for P, alpha, M, K in large:
-            if K not in qs:
-                qs[K] = bn.quant_act(synth.tokens_bf16_torch(N, K, 17 + K))
-            q = qs[K]
-            bufs.append((P, alpha, q, torch.empty((N, M), dtype=torch.int32, device="cuda"),
-                         torch.empty((N, M), dtype=torch.float32, device="cuda"), M, K))
+        for groups in layers:
+            for K, mats in groups:
+                x = synth.tokens_bf16_torch(N, K, 17 + K)
+                q = bn.quant_act(x)
+                outs = [(torch.empty((N, P.shape[0]), dtype=torch.int32, device="cuda"),
+                         torch.empty((N, P.shape[0]), dtype=torch.float32, device="cuda"))
+                        for P, _ in mats]
+                qout = q if N > 8 else None
+                bufs.append((x, q, mats, outs, qout))
 
-        def run(bufs=bufs):
-            for P, alpha, q, d, yy, M, K in bufs:
-                bn.gemv(P, alpha, q[0], q[1], q[2], out=(d, yy))
+        def run(bufs=bufs, how=how):
+            for x, q, mats, outs, qout in bufs:
+                if how == "linear":
+                    bn.linear(x, mats, out=outs, qout=qout)
+                else:
+                    for (P, a), o in zip(mats, outs):
+                        bn.gemv(P, a, q[0], q[1], q[2], out=o)
         g = capture(torch, run)
         t = time_graph(torch, g, 5, 2) / 5
-        byts = sum(M * K // 4 + N * K + N * M * 8 for P, a, q, d, yy, M, K in bufs)
-        rows[f"large_N{N}"] = {"workload": "large layer stack, 8 layers x 7 GEMVs, 1.71 GB packed",
-                               "us_per_step": round(t * 1e6, 1),
-                               "GB/s": round(byts / t / 1e9, 1),
-                               "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
-                               "tokens_per_s": round(N / t, 1)}
-        del bufs, g
-    del large
+        del g
+        K_tok = sum(x.shape[1] for x, q, mats, outs, qout in bufs)
+        M_out = sum(P.shape[0] for x, q, mats, outs, qout in bufs for P, _ in mats)
+        tok_bytes = N * K_tok * (2 if how == "linear" else 1)
+        byts = packed + tok_bytes + N * M_out * 8
+        tag = f"large_N{N}" + ("" if how == "linear" else "_per_matrix_gemv")
+        rows[tag] = {"workload": "large layer stack, 8 layers x 7 projections, 1.71 GB packed",
+                     "launches_per_step": len(bufs) if how == "linear" else 56,
+                     "us_per_step": round(t * 1e6, 1), "GB/s": round(byts / t / 1e9, 1),
+                     "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "tokens_per_s": round(N / t, 1)}
+        del bufs
+    del layers
     return rows
 
 
@@ -477,7 +499,7 @@ def main():
                    "graph": True,
                    "eager_ms_per_step": round(eager_ms, 3),
                    "unfused_graph_ms_per_step": round(unfused_ms, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_valu_kernel<1,PF,2> (fused bf16 quantise + GEMV)",
+        "roofline": {"bound": "hbm", "kernel": "gemv_valu_kernel<1,LPR,2,JM> (fused bf16 quantise + GEMV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(per_launch_s * 1e6, 3)},
