@@ -263,12 +263,20 @@ static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8
 
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    // Token tile matched to small N so no MFMA column work is wasted.  For
-    // larger N, 128x128 tiles of four waves: eight-wave tiles (128x128 and
-    // 256x128) and three or four stages measured within 5% of it on the
-    // 0.6B-class layer.
+    // Token tile matched to small N so no MFMA column work is wasted.
     if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    // The K loop is bound by the LDS-DMA fills (removing its MFMAs leaves
+    // three quarters of its time), so larger tiles -- more MFMA work per
+    // staged byte -- win where there are enough of them: 256x128 tiles of
+    // eight waves (64x64 each; 24 KB per block for 128 MFMAs against 20 KB for
+    // 64 at 128x128) when a launch has at least two per CU (the grouped
+    // q/k/v and gate/up launches of a layer), 128x128 tiles of four waves
+    // otherwise.  256x256 tiles measured slower.
+    int64_t big = 0;
+    for (int i = 0; i < nmats; ++i) big += (mats[i].M + 255) / 256;
+    big *= (N + 127) / 128;
+    if (big >= 512) return run_gemm<256, 128, 4, 2, 3>(mats, nmats, K, xq, xs, xsum, N, st);
     return run_gemm<128, 128, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 

@@ -520,3 +520,13 @@ def test_pack_f32_rejects_non_finite(bn):
     with pytest.raises(bn.BitnetError) as e:
         bn.pack_f32(dev(W))
     assert e.value.status == 5
+
+
+def test_gemm_group_large_tiles_ragged(bn):
+    """A group large enough for the 256x128 tiles (512 of them), with M and N
+    that are not multiples of the tile: every row against the per-matrix GEMM
+    (128x128 tiles), sampled rows against the oracle."""
+    Ms, K, N = (2500, 1300), 256, 4000
+    assert sum((M + 255) // 256 for M in Ms) * ((N + 127) // 128) >= 512
+    run_gemm_group(bn, Ms, K, N, seed=4242,
+                   rows=[(0, 16), (1284, 16)], want_dot=True)
