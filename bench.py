@@ -318,9 +318,10 @@ def row_decode(bn, synth, torch, stack):
 
 def row_large(bn, synth, torch, stack):
     """a3 at streaming sizes: the large-layer stack (8 layers x 7 projections,
-    1.71 GB packed, streamed from HBM every step) at N = 1 and 16, one fused
-    quantise + GEMV launch per dependency group (q/k/v, o, gate/up, down) on
-    bf16 tokens; at N = 1 also the per-matrix GEMV on int8 tokens."""
+    1.71 GB packed, streamed from HBM every step).  N = 1: one grouped GEMV
+    launch per dependency group (q/k/v, o, gate/up, down) on int8 tokens;
+    also the fused quantise + GEMV on bf16 tokens and the per-matrix GEMV.
+    N = 16: quantiser + batched decode per group (bitnet_linear_i2s)."""
     rows = {}
     layers = []
     for l in range(8):
@@ -336,7 +337,7 @@ def row_large(bn, synth, torch, stack):
             groups.append((K, mats))
         layers.append(groups)
     packed = sum(P.numel() for groups in layers for K, mats in groups for P, _ in mats)
-    for N, how in ((1, "linear"), (1, "gemv"), (16, "linear")):
+    for N, how in ((1, "group"), (1, "linear"), (1, "gemv"), (16, "linear")):
         bufs = []
         for groups in layers:
             for K, mats in groups:
@@ -352,6 +353,8 @@ def row_large(bn, synth, torch, stack):
             for x, q, mats, outs, qout in bufs:
                 if how == "linear":
                     bn.linear(x, mats, out=outs, qout=qout)
+                elif how == "group":
+                    bn.gemv_group(mats, q[0], q[1], q[2], out=outs)
                 else:
                     for (P, a), o in zip(mats, outs):
                         bn.gemv(P, a, q[0], q[1], q[2], out=o)
@@ -362,9 +365,13 @@ def row_large(bn, synth, torch, stack):
         M_out = sum(P.shape[0] for x, q, mats, outs, qout in bufs for P, _ in mats)
         tok_bytes = N * K_tok * (2 if how == "linear" else 1)
         byts = packed + tok_bytes + N * M_out * 8
-        tag = f"large_N{N}" + ("" if how == "linear" else "_per_matrix_gemv")
+        tag = f"large_N{N}" + ("" if how == "group" or N > 8 else
+                               {"linear": "_fused_bf16", "gemv": "_per_matrix"}[how])
         rows[tag] = {"workload": "large layer stack, 8 layers x 7 projections, 1.71 GB packed",
-                     "launches_per_step": len(bufs) if how == "linear" else 56,
+                     "launches": {"group": "32 grouped GEMV, int8 tokens",
+                                  "linear": ("32 fused quantise + GEMV, bf16 tokens" if N <= 8 else
+                                             "32 x (quantiser + batched-decode GEMV), bf16 tokens"),
+                                  "gemv": "56 GEMV, int8 tokens"}[how],
                      "us_per_step": round(t * 1e6, 1), "GB/s": round(byts / t / 1e9, 1),
                      "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
                      "tokens_per_s": round(N / t, 1)}

@@ -164,6 +164,21 @@ int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
                       float *x_scale, int32_t *x_sum, void *stream);
 
 /*
+ * bitnet_gemv_i2s_i8_group -- decode matmul (N <= BITNET_GEMV_MAX_N tokens,
+ * already quantised) of several I2_S matrices that share the tokens: one
+ * vector-ALU launch for all of them when N <= 2, else the batched-decode MFMA
+ * kernel per matrix.  [P1 §2-1, §4-3; P2 §3; P3 §3.2]
+ *
+ *   mats, xq, x_scale, x_sum   as bitnet_gemm_i2s_i8_group.
+ *
+ * Outputs equal bitnet_gemv_i2s_i8 on each matrix, bit for bit.
+ * 0 <= N <= BITNET_GEMV_MAX_N; N == 0 or all M == 0 is a no-op.
+ */
+int bitnet_gemv_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
+                             const int8_t *xq, const float *x_scale,
+                             const int32_t *x_sum, int64_t N, void *stream);
+
+/*
  * bitnet_gemm_i2s_i8_group -- prefill matmul of several I2_S matrices that
  * share one block of quantised tokens, in one MFMA launch (e.g. q/k/v, or
  * gate/up, of a layer).  [P1 §4-5 (a separate prefill path), §4-3 (one

@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
     L.bitnet_gemm_i2s_i8_group.argtypes = [ctypes.POINTER(I2SMatrix), ctypes.c_int, i64, p, p, p,
                                            i64, p]
     L.bitnet_gemm_i2s_i8_group.restype = ctypes.c_int
+    L.bitnet_gemv_i2s_i8_group.argtypes = L.bitnet_gemm_i2s_i8_group.argtypes
+    L.bitnet_gemv_i2s_i8_group.restype = ctypes.c_int
     L.bitnet_absmean_i2s.argtypes = [p, ctypes.c_int, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
     L.bitnet_absmean_i2s.restype = ctypes.c_int
     L.bitnet_pack_i2s_f32.argtypes = [p, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
@@ -219,6 +221,16 @@ def gemm_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     N, K = xq.shape
     out = _mats_out(mats, N, xq.device, want_dot, want_y, out)
     _check(load().bitnet_gemm_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
+                                           _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
+    return out
+
+
+def gemv_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
+    """Decode matmul (N <= 64 quantised tokens) of every (packed, w_scale) in
+    ``mats`` -> [(dot | None, y | None) per matrix]."""
+    N, K = xq.shape
+    out = _mats_out(mats, N, xq.device, want_dot, want_y, out)
+    _check(load().bitnet_gemv_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
                                            _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
     return out
 

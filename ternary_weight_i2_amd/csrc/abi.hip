@@ -293,6 +293,41 @@ static int check_mats(const char *fn, const bitnet_i2s_matrix *mats, int n_mats)
     return BITNET_OK;
 }
 
+BITNET_API int bitnet_gemv_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
+                                        const int8_t *xq, const float *x_scale,
+                                        const int32_t *x_sum, int64_t N, void *stream) {
+    const char *fn = "bitnet_gemv_i2s_i8_group";
+    if (int s = check_mats(fn, mats, n_mats)) return s;
+    if (N < 0 || N > BITNET_GEMV_MAX_N)
+        return fail(BITNET_E_SHAPE, "%s: N=%lld outside [0, %d]", fn, (long long)N,
+                    BITNET_GEMV_MAX_N);
+    if (int s = check_k(fn, K)) return s;
+    int64_t rows = 0;
+    for (int i = 0; i < n_mats; ++i) rows += mats[i].M;
+    if (N == 0 || rows == 0) return ok();
+    if (!xq || !x_scale || !x_sum)
+        return fail(BITNET_E_NULL, "%s: xq, x_scale and x_sum are required", fn);
+    if (!aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+        return fail(BITNET_E_ALIGN, "%s: xq must be 16-byte and x_scale/x_sum 4-byte aligned", fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (N <= BITNET_VALU_MAX_N) {
+        bitnet::GemvMat gm[bitnet::kMaxMats];
+        for (int i = 0; i < n_mats; ++i)
+            gm[i] = bitnet::GemvMat{mats[i].packed, mats[i].dot, mats[i].y, mats[i].w_scale,
+                                    (int)mats[i].M, 0};
+        e = bitnet::launch_gemv_valu(gm, n_mats, K, N, 0, xq, x_scale, x_sum, nullptr, nullptr,
+                                     nullptr, st);
+    } else {
+        for (int i = 0; i < n_mats && e == hipSuccess; ++i)
+            if (mats[i].M > 0)
+                e = bitnet::launch_gemv_mfma(mats[i].packed, mats[i].w_scale, mats[i].M, K, xq,
+                                             x_scale, x_sum, N, mats[i].dot, mats[i].y, st);
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 BITNET_API int bitnet_gemm_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
                                         const int8_t *xq, const float *x_scale,
                                         const int32_t *x_sum, int64_t N, void *stream) {

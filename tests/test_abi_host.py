@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     fns = set(declared_functions())
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
-            "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_linear_i2s",
+            "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_gemv_i2s_i8_group",
+            "bitnet_linear_i2s",
             "bitnet_absmean_i2s", "bitnet_pack_i2s_f32", "bitnet_last_error",
             "bitnet_abi_version"} <= fns
 
@@ -151,9 +152,11 @@ def test_linear_validation(L):
              None, None, None, None) == OK
 
 
-def test_gemm_group_validation(L):
+@pytest.mark.parametrize("name,maxn", [("bitnet_gemm_i2s_i8_group", 1 << 21),
+                                       ("bitnet_gemv_i2s_i8_group", 64)])
+def test_group_validation(L, name, maxn):
     from ternary_weight_i2_amd._binding import I2SMatrix
-    f = L.bitnet_gemm_i2s_i8_group
+    f = getattr(L, name)
 
     def mats(*ms):
         arr = (I2SMatrix * len(ms))()
@@ -167,7 +170,7 @@ def test_gemm_group_validation(L):
     assert f(None, 1, 256, FAKE, FAKE, FAKE, 4, None) == E_NULL
     assert f(g1, 1, 200, FAKE, FAKE, FAKE, 4, None) == E_SHAPE
     assert f(g1, 1, 256, FAKE, FAKE, FAKE, -1, None) == E_SHAPE
-    assert f(g1, 1, 256, FAKE, FAKE, FAKE, (1 << 21) + 1, None) == E_SHAPE
+    assert f(g1, 1, 256, FAKE, FAKE, FAKE, maxn + 1, None) == E_SHAPE
     assert f(g1, 1, 256, None, FAKE, FAKE, 4, None) == E_NULL
     assert f(g1, 1, 256, FAKE, None, FAKE, 4, None) == E_NULL
     assert f(g1, 1, 256, MIS, FAKE, FAKE, 4, None) == E_ALIGN
@@ -182,7 +185,7 @@ def test_gemm_group_validation(L):
              None) == E_ALIGN
     assert f(mats(I2SMatrix(FAKE, -2, 0.1, FAKE, FAKE)), 1, 256, FAKE, FAKE, FAKE, 4,
              None) == E_SHAPE
-    assert "bitnet_gemm_i2s_i8_group" in _err(L)
+    assert name in _err(L)
     # no-ops: N == 0, or every matrix empty
     assert f(g1, 1, 256, None, None, None, 0, None) == OK
     assert f(mats(I2SMatrix(None, 0, 0.1, None, None)), 1, 256, None, None, None, 4, None) == OK

@@ -530,3 +530,30 @@ def test_gemm_group_large_tiles_ragged(bn):
     assert sum((M + 255) // 256 for M in Ms) * ((N + 127) // 128) >= 512
     run_gemm_group(bn, Ms, K, N, seed=4242,
                    rows=[(0, 16), (1284, 16)], want_dot=True)
+
+
+@pytest.mark.parametrize("Ms,K,N", [((5, 0, 130), 128, 1), ((640, 640, 2560), 2560, 2),
+                                    ((257, 33), 384, 7), ((100, 200), 640, 64)])
+def test_gemv_group(bn, Ms, K, N):
+    """Grouped decode GEMV vs bitnet_gemv_i2s_i8 per matrix (bit for bit) and
+    the oracle."""
+    rng = np.random.default_rng(sum(Ms) + K + N)
+    Ws = [synth.ternary(rng, M, K) for M in Ms]
+    alphas = [synth.weight_scale(rng) for _ in Ms]
+    x = synth.tokens_bf16(rng, N, K)
+    xq, xs, xsum = bn.quant_act(to_bf16_tensor(x))
+    Ps = [bn.pack(dev(W)) for W in Ws]
+    outs = bn.gemv_group(list(zip(Ps, alphas)), xq, xs, xsum)
+    torch.cuda.synchronize()
+    q, s, qs = oracle.quant_act(x)
+    for W, P, alpha, (d, y) in zip(Ws, Ps, alphas, outs):
+        if W.shape[0] == 0:
+            continue
+        d2, y2 = bn.gemv(P, alpha, xq, xs, xsum)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(d.cpu().numpy(), d2.cpu().numpy())
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+        Pr, _ = oracle.pack_i2s(W)
+        D, _ = oracle.linear_i2s(Pr, K, q, s, alpha, nthreads=8, want_y=False)
+        np.testing.assert_array_equal(d.cpu().numpy(), D)
+        check_y(y.cpu().numpy(), D, alpha, s)
