@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.orc_absmean_ternary_bf16.argtypes = [_p, _i64, ctypes.c_float, _p]
         L.orc_sign_ternary_f32.argtypes = [_p, _i64, _p, _p]
         L.orc_sign_ternary_f32.restype = _i64
+        L.orc_ffn_act_quant.argtypes = [_p, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p]
         L.orc_quant_act_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
         L.orc_quant_act_f32.restype = None
         L.orc_quant_act_bf16.argtypes = [_p, _i64, _i64, _p, _p, _p]
@@ -255,3 +256,21 @@ def sign_ternary(w: np.ndarray) -> tuple[np.ndarray, float, int]:
     wmax = ctypes.c_float(0.0)
     bad = lib().orc_sign_ternary_f32(_ptr(w), w.size, _ptr(q), ctypes.byref(wmax))
     return q, float(np.float32(wmax.value)), int(bad)
+
+
+def ffn_act_quant(g: np.ndarray, u: np.ndarray, gamma, eps: float):
+    """sqrelu(g) * u -> RMS sub-norm (binary64 sum of squares in 32-channel
+    runs, gain gamma or 1) -> per-token int8 quantisation [P4 "Forward Pass";
+    P1 §4-5].  g, u: fp32 [N][F].  Returns (q, s, qsum, v)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    N, F = g.shape
+    assert u.shape == (N, F) and F % 32 == 0
+    gm = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float32)
+    q = np.empty((N, F), dtype=np.int8)
+    s = np.empty((N,), dtype=np.float32)
+    qs = np.empty((N,), dtype=np.int32)
+    v = np.empty((N, F), dtype=np.float32)
+    lib().orc_ffn_act_quant(_ptr(g), _ptr(u), None if gm is None else _ptr(gm),
+                            np.float32(eps), N, F, _ptr(q), _ptr(s), _ptr(qs), _ptr(v))
+    return q, s, qs, v

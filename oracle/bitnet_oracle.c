@@ -325,3 +325,39 @@ int64_t orc_sign_ternary_f32(const float *w, int64_t n, int8_t *q, float *wmax)
     if (wmax) *wmax = m;
     return bad;
 }
+
+/* ---- squared-ReLU gated FFN activation + sub-norm + quantisation ---- */
+
+void orc_ffn_act_quant(const float *g, const float *u, const float *gamma, float eps,
+                       int64_t N, int64_t F, int8_t *q, float *s, int32_t *qsum,
+                       float *v)
+{
+    float *h = malloc((size_t)F * sizeof *h);
+    float *nv = malloc((size_t)F * sizeof *nv);
+    for (int64_t n = 0; n < N; n++) {
+        const float *gn = g + n * F, *un = u + n * F;
+        /* [P4]: sqrelu(gate) (x) up -- squared ReLU of the gate times up */
+        for (int64_t k = 0; k < F; k++) {
+            float r = gn[k] > 0.0f ? gn[k] : 0.0f;
+            float r2 = r * r;
+            h[k] = r2 * un[k];
+        }
+        /* ffn_sub_norm: RMS normalisation over the F channels; binary64
+         * accumulation of the (exact) squares in the stated order */
+        double ss = 0.0;
+        for (int64_t c0 = 0; c0 < F; c0 += 32) {
+            double part = 0.0;
+            for (int64_t k = c0; k < c0 + 32; k++) part += (double)h[k] * (double)h[k];
+            ss += part;
+        }
+        float c = (float)(1.0 / sqrt(ss / (double)F + (double)eps));
+        for (int64_t k = 0; k < F; k++) {
+            float t = h[k] * c;
+            nv[k] = gamma ? t * gamma[k] : t;
+        }
+        if (v) memcpy(v + n * F, nv, (size_t)F * sizeof *nv);
+        quant_row(nv, F, q + n * F, s + n, qsum + n);
+    }
+    free(h);
+    free(nv);
+}

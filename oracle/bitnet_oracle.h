@@ -106,6 +106,20 @@ void orc_absmean_ternary_bf16(const uint16_t *w, int64_t n, float alpha, int8_t 
  * number of non-finite weights (their q is left 0). */
 int64_t orc_sign_ternary_f32(const float *w, int64_t n, int8_t *q, float *wmax);
 
+/* Squared-ReLU gated FFN activation feeding the down projection [P4
+ * "Forward Pass": inner = ffn_sub_norm(sqrelu(gate(x)) (x) up(x)),
+ * out = down(inner)], per token n over F channels (F a multiple of 32):
+ *   r_k = max(g_k, 0);  h_k = (r_k * r_k) * u_k                    (fp32)
+ *   ss  = sum of h_k^2 in binary64 -- each run of 32 consecutive channels
+ *         summed in index order, then the run sums in index order
+ *   c   = fp32(1 / sqrt(ss / F + eps))   (binary64, one final rounding)
+ *   v_k = (h_k * c) * gamma_k            (fp32; gamma NULL means 1)
+ * then v is quantised per token exactly as orc_quant_act_f32 does.
+ * v (if not NULL) receives the normalised activations [N][F]. */
+void orc_ffn_act_quant(const float *g, const float *u, const float *gamma, float eps,
+                       int64_t N, int64_t F, int8_t *q, float *s, int32_t *qsum,
+                       float *v);
+
 #ifdef __cplusplus
 }
 #endif

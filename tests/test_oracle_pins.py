@@ -502,3 +502,73 @@ def test_sign_ternary_of_scaled_ternary_round_trips(orc):
     q, wmax, bad = orc.sign_ternary(W)
     np.testing.assert_array_equal(q, T)
     assert bad == 0 and wmax == np.float32(0.0731)
+
+
+# ------------------------------------------- squared-ReLU gated FFN glue
+def _rms_ref(h, gamma, eps):
+    """h / sqrt(mean(h^2) + eps) * gamma, float64 (numpy's own sum order)."""
+    h = h.astype(np.float64)
+    r = h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + eps)
+    return r if gamma is None else r * gamma.astype(np.float64)
+
+
+def test_ffn_sqrelu_gate_and_norm(orc):
+    """[P4 "Forward Pass"]: sqrelu(gate) (x) up, then the sub-norm: channels
+    with gate <= 0 are exactly zero, the rest follow h / rms(h) * gamma."""
+    rng = np.random.default_rng(11)
+    N, F = 3, 256
+    g = rng.standard_normal((N, F)).astype(np.float32)
+    u = rng.standard_normal((N, F)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, F).astype(np.float32)
+    q, s, qs, v = orc.ffn_act_quant(g, u, gamma, 1e-5)
+    assert (v[g <= 0] == 0).all() and (q[g <= 0] == 0).all()
+    h = np.maximum(g, 0).astype(np.float64) ** 2 * u
+    np.testing.assert_allclose(v, _rms_ref(h, gamma, 1e-5), rtol=2e-6, atol=1e-30)
+    # the quantisation step is the activation quantiser's
+    q2, s2, qs2 = orc.quant_act(v)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(s.view(np.uint32), s2.view(np.uint32))
+    np.testing.assert_array_equal(qs, qs2)
+
+
+def test_ffn_unit_rms_and_constant_rows(orc):
+    rng = np.random.default_rng(12)
+    g = np.abs(rng.standard_normal((4, 512))).astype(np.float32) + 0.1
+    u = rng.standard_normal((4, 512)).astype(np.float32)
+    _, _, _, v = orc.ffn_act_quant(g, u, None, 0.0)
+    np.testing.assert_allclose(np.mean(v.astype(np.float64) ** 2, axis=1), 1.0, rtol=1e-6)
+    g = np.full((2, 128), 0.75, np.float32)
+    u = np.ones((2, 128), np.float32)
+    q, s, qs, v = orc.ffn_act_quant(g, u, None, 0.0)
+    np.testing.assert_allclose(v, 1.0, rtol=1.2e-7)
+    assert (q == 127).all() and (qs == 127 * 128).all()
+
+
+def test_ffn_power_of_two_invariances(orc):
+    """Scaling the gate by 2 scales h by exactly 4 and the sum of squares by
+    16, so (eps = 0) the normalised values and codes are unchanged bit for
+    bit; doubling gamma doubles v and halves s exactly."""
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal((5, 384)).astype(np.float32)
+    u = rng.standard_normal((5, 384)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, 384).astype(np.float32)
+    q, s, qs, v = orc.ffn_act_quant(g, u, gamma, 0.0)
+    q2, s2, qs2, v2 = orc.ffn_act_quant(g * np.float32(2), u, gamma, 0.0)
+    np.testing.assert_array_equal(v, v2)
+    np.testing.assert_array_equal(q, q2)
+    q3, s3, qs3, v3 = orc.ffn_act_quant(g, u, gamma * np.float32(2), 0.0)
+    np.testing.assert_array_equal(v3, v * np.float32(2))
+    np.testing.assert_array_equal(q3, q)
+    np.testing.assert_array_equal(s3, s / np.float32(2))
+
+
+def test_ffn_eps_dominates_tiny_activations(orc):
+    g = np.full((1, 128), 1e-3, np.float32)
+    u = np.ones((1, 128), np.float32)
+    _, _, _, v = orc.ffn_act_quant(g, u, None, 1e-5)
+    h = np.float64(np.float32(1e-3)) ** 2
+    np.testing.assert_allclose(v, h / np.sqrt(h * h + 1e-5), rtol=2e-7)
+    # a token whose gate is never positive normalises to zero (eps > 0)
+    q, s, qs, v = orc.ffn_act_quant(-np.abs(g), u, None, 1e-5)
+    assert not v.any() and not q.any() and qs[0] == 0
+    assert s[0] == np.float32(127.0 / 1e-5)
