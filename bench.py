@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the secondary per-row measurements")
-    ap.add_argument("--only", choices=("pack", "convert", "quant", "decode", "large", "prefill"),
+    ap.add_argument("--only", choices=("pack", "convert", "quant", "decode", "large", "prefill",
+                                       "ffn"),
                     help="run only this group of secondary rows and print them (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
@@ -225,7 +226,8 @@ def secondary_rows(bn, synth, torch, stack, only=None):
     fresh on the device.  ``only`` picks one group of rows."""
     rows = {}
     parts = {"pack": row_pack, "convert": row_convert, "quant": row_quant,
-             "decode": row_decode, "large": row_large, "prefill": row_prefill}
+             "decode": row_decode, "large": row_large, "prefill": row_prefill,
+             "ffn": row_ffn}
     for name, fn in parts.items():
         if only is None or only == name:
             rows.update(fn(bn, synth, torch, stack))
@@ -268,6 +270,58 @@ def row_convert(bn, synth, torch, stack):
     rows["pack_f32"] = {"shape": f"{M}x{K} fp32", "us": round(t * 1e6, 2),
                         "GB/s": round((M * K * 4 + M * K // 4) / t / 1e9, 1),
                         "note": "includes the stream sync"}
+    return rows
+
+
+def row_ffn(bn, synth, torch, stack):
+    """NEXT f3: the 2B-class squared-ReLU gated FFN block per layer -- fused
+    gate/up launch, the activation + sub-norm + quantise kernel, then down --
+    over 30 layers (weights from HBM), N = 1 and 128 tokens."""
+    rows = {}
+    F, H = synth.SHAPES["b2"]["gate"]
+    layers = []
+    for l in range(30):
+        mats = {}
+        for p in ("gate", "up", "down"):
+            M, K = synth.SHAPES["b2"][p]
+            mats[p] = (bn.pack(synth.ternary_torch(M, K, synth.stack_seed("b2", l, p, "weights"))),
+                       synth.weight_scale(synth.rng_for("b2", l, p, "scale")))
+        gamma = torch.rand(F, device="cuda") + 0.5
+        layers.append((mats, gamma))
+    for N in (1, 128):
+        x = synth.tokens_bf16_torch(N, H, 23 + N)
+        bufs = []
+        for mats, gamma in layers:
+            gu = [(None, torch.empty((N, F), dtype=torch.float32, device="cuda")) for _ in range(2)]
+            q = (torch.empty((N, F), dtype=torch.int8, device="cuda"),
+                 torch.empty((N,), dtype=torch.float32, device="cuda"),
+                 torch.empty((N,), dtype=torch.int32, device="cuda"))
+            qx = (torch.empty((N, H), dtype=torch.int8, device="cuda"),
+                  torch.empty((N,), dtype=torch.float32, device="cuda"),
+                  torch.empty((N,), dtype=torch.int32, device="cuda"))
+            out = (torch.empty((N, H), dtype=torch.int32, device="cuda"),
+                   torch.empty((N, H), dtype=torch.float32, device="cuda"))
+            bufs.append((mats, gamma, gu, q, qx, out))
+
+        def run(bufs=bufs, N=N):
+            for mats, gamma, gu, q, qx, out in bufs:
+                bn.linear(x, [mats["gate"], mats["up"]], out=gu, qout=qx if N > 8 else None)
+                bn.ffn_act_quant(gu[0][1], gu[1][1], gamma, 1e-5, out=q)
+                P, a = mats["down"]
+                if N <= 64:
+                    bn.gemv(P, a, q[0], q[1], q[2], out=out)
+                else:
+                    bn.gemm(P, a, q[0], q[1], q[2], out=out)
+        g = capture(torch, run)
+        t = time_graph(torch, g, 10, 3) / 10
+        del g
+        wbytes = sum(m[p][0].numel() for m, _ in layers for p in ("gate", "up", "down"))
+        byts = wbytes + 30 * N * (2 * H + 2 * F * 4 + F * 4 + 2 * F + H * 8)
+        rows[f"ffn_N{N}"] = {"workload": "2B-class FFN block (gate/up, sqrelu + sub-norm + quantise, down) x 30 layers",
+                             "launches_per_step": 90, "us_per_step": round(t * 1e6, 1),
+                             "GB/s": round(byts / t / 1e9, 1),
+                             "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del bufs
     return rows
 
 

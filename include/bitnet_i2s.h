@@ -164,6 +164,27 @@ int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
                       float *x_scale, int32_t *x_sum, void *stream);
 
 /*
+ * bitnet_ffn_act_quant_i8 -- the squared-ReLU gated FFN activation that feeds
+ * the down projection, quantised for it.  [P4 "Forward Pass":
+ * inner = ffn_sub_norm(sqrelu(gate(x)) * up(x)), out = down(inner); P1 §4-5]
+ *
+ *   g, u     device [N][F] fp32: the gate and up projections' y outputs
+ *            (16-byte aligned); F a multiple of 128, F <= BITNET_MAX_K.
+ *   gamma    device [F] fp32 gain of the sub-norm (16-byte aligned), or NULL for 1.
+ *   eps      the sub-norm's epsilon (positive, finite; else BITNET_E_VALUE).
+ *   xq, x_scale, x_sum   outputs as bitnet_quant_act_i8 writes them, ready
+ *            for bitnet_gemv_i2s_i8 / bitnet_gemm_i2s_i8 with the down weights.
+ *
+ * Per token: h = (relu(g)^2) * u in fp32; ss = sum of h^2 in binary64 over
+ * runs of 32 channels in index order, then the run sums in index order;
+ * c = fp32(1 / sqrt(ss / F + eps)); v = (h * c) * gamma in fp32; then per-token
+ * absmax int8 quantisation of v.  0 <= N < 2^31; N == 0 is a no-op.
+ */
+int bitnet_ffn_act_quant_i8(const float *g, const float *u, const float *gamma, float eps,
+                            int64_t N, int64_t F, int8_t *xq, float *x_scale,
+                            int32_t *x_sum, void *stream);
+
+/*
  * bitnet_gemv_i2s_i8_group -- decode matmul (N <= BITNET_GEMV_MAX_N tokens,
  * already quantised) of several I2_S matrices that share the tokens: one
  * vector-ALU launch for all of them when N <= 2, else the batched-decode MFMA

@@ -6,6 +6,6 @@ torch tensors into that ABI; it loads the library lazily and raises if it
 is missing -- there is no fallback path.
 """
 from ._binding import (  # noqa: F401
-    BitnetError, I2SMatrix, abi_version, absmean_pack, gemm, gemm_group, gemv, gemv_group,
-    lib_path, linear, load, pack, pack_f32, quant_act,
+    BitnetError, I2SMatrix, abi_version, absmean_pack, ffn, ffn_act_quant, gemm, gemm_group,
+    gemv, gemv_group, lib_path, linear, load, pack, pack_f32, quant_act,
 )

@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
     L.bitnet_gemm_i2s_i8_group.restype = ctypes.c_int
     L.bitnet_gemv_i2s_i8_group.argtypes = L.bitnet_gemm_i2s_i8_group.argtypes
     L.bitnet_gemv_i2s_i8_group.restype = ctypes.c_int
+    L.bitnet_ffn_act_quant_i8.argtypes = [p, p, p, f32, i64, i64, p, p, p, p]
+    L.bitnet_ffn_act_quant_i8.restype = ctypes.c_int
     L.bitnet_absmean_i2s.argtypes = [p, ctypes.c_int, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
     L.bitnet_absmean_i2s.restype = ctypes.c_int
     L.bitnet_pack_i2s_f32.argtypes = [p, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
@@ -233,6 +235,38 @@ def gemv_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     _check(load().bitnet_gemv_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
                                            _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
     return out
+
+
+def ffn_act_quant(g, u, gamma=None, eps=1e-5, out=None):
+    """sqrelu(g) * u -> RMS sub-norm (gain gamma or 1, eps) -> int8 tokens for
+    the down projection: fp32 g, u [N][F] (cuda) -> (xq, s, xsum)."""
+    import torch
+    if g.dtype != torch.float32 or u.dtype != torch.float32 or g.shape != u.shape or g.dim() != 2:
+        raise TypeError("g and u must be float32 tensors of the same 2-D shape")
+    N, F = g.shape
+    if out is None:
+        out = (torch.empty((N, F), dtype=torch.int8, device=g.device),
+               torch.empty((N,), dtype=torch.float32, device=g.device),
+               torch.empty((N,), dtype=torch.int32, device=g.device))
+    xq, xs, xsum = out
+    _check(load().bitnet_ffn_act_quant_i8(_ptr(g), _ptr(u), _ptr(gamma), float(eps), N, F,
+                                          _ptr(xq), _ptr(xs), _ptr(xsum), _stream(g)))
+    return xq, xs, xsum
+
+
+def ffn(x, gate, up, down, gamma=None, eps=1e-5):
+    """The squared-ReLU gated FFN block on I2_S weights, as three library calls:
+    bitnet_linear_i2s(x, [gate, up]) -> bitnet_ffn_act_quant_i8 -> the down
+    projection (decode or prefill kernel by N).  gate/up/down are
+    (packed, w_scale) pairs; x is fp32/bf16 [N][K] (cuda).
+    Returns (dot, y) of the down projection."""
+    outs, _ = linear(x, [gate, up])
+    (_, g), (_, u) = outs
+    xq, xs, xsum = ffn_act_quant(g, u, gamma, eps)
+    P, ws = down
+    if xq.shape[0] <= GEMV_MAX_N:
+        return gemv(P, ws, xq, xs, xsum)
+    return gemm(P, ws, xq, xs, xsum)
 
 
 def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):

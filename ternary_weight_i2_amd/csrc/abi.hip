@@ -293,6 +293,27 @@ static int check_mats(const char *fn, const bitnet_i2s_matrix *mats, int n_mats)
     return BITNET_OK;
 }
 
+BITNET_API int bitnet_ffn_act_quant_i8(const float *g, const float *u, const float *gamma,
+                                      float eps, int64_t N, int64_t F, int8_t *xq,
+                                      float *x_scale, int32_t *x_sum, void *stream) {
+    const char *fn = "bitnet_ffn_act_quant_i8";
+    if (N < 0) return fail(BITNET_E_SHAPE, "%s: negative N=%lld", fn, (long long)N);
+    if (N > 0x7fffffffLL) return fail(BITNET_E_SHAPE, "%s: N=%lld exceeds 2^31-1", fn, (long long)N);
+    if (int s = check_k(fn, F)) return s;
+    if (!(eps > 0.0f) || !(eps < 3.4e38f))
+        return fail(BITNET_E_VALUE, "%s: eps must be positive and finite", fn);
+    if (N == 0) return ok();
+    if (!g || !u || !xq || !x_scale || !x_sum)
+        return fail(BITNET_E_NULL, "%s: g, u, xq, x_scale and x_sum are required", fn);
+    if (!aligned(g, 16) || !aligned(u, 16) || (gamma && !aligned(gamma, 16)) ||
+        !aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(x_sum, 4))
+        return fail(BITNET_E_ALIGN, "%s: g, u, gamma and xq must be 16-byte aligned", fn);
+    hipError_t e = bitnet::launch_ffn_act_quant(g, u, gamma, eps, N, F, xq, x_scale, x_sum,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 BITNET_API int bitnet_gemv_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t K,
                                         const int8_t *xq, const float *x_scale,
                                         const int32_t *x_sum, int64_t N, void *stream) {

@@ -174,6 +174,12 @@ struct GemmArgs {
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st);
 
+// Squared-ReLU gated FFN activation + sub-norm + int8 quantisation, one
+// workgroup per token (F a multiple of 128, at most 32768).
+hipError_t launch_ffn_act_quant(const float *g, const float *u, const float *gamma, float eps,
+                                int64_t N, int64_t F, int8_t *xq, float *xs, int32_t *xsum,
+                                hipStream_t st);
+
 // One-time weight conversion (AbsMean ternariser, sign/threshold packer).
 constexpr int kConvPartials = 1024;   // partial sums of the AbsMean reduction
 hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, double *partial,

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
             "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_gemv_i2s_i8_group",
             "bitnet_linear_i2s",
-            "bitnet_absmean_i2s", "bitnet_pack_i2s_f32", "bitnet_last_error",
+            "bitnet_absmean_i2s", "bitnet_pack_i2s_f32", "bitnet_ffn_act_quant_i8",
+            "bitnet_last_error",
             "bitnet_abi_version"} <= fns
 
 
@@ -216,6 +217,24 @@ def test_conversion_validation(L):
     a.value = 7.0
     assert g(None, 0, 128, None, ctypes.byref(a), None) == OK and a.value == 0.0
     assert _err(L) == ""
+
+
+def test_ffn_act_quant_validation(L):
+    f = L.bitnet_ffn_act_quant_i8
+    assert f(FAKE, FAKE, None, 1e-5, -1, 256, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, None, 1e-5, 2, 200, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, None, 1e-5, 2, 32768 + 128, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert f(FAKE, FAKE, None, 0.0, 2, 256, FAKE, FAKE, FAKE, None) == E_VALUE
+    assert f(FAKE, FAKE, None, -1e-5, 2, 256, FAKE, FAKE, FAKE, None) == E_VALUE
+    assert f(FAKE, FAKE, None, float("inf"), 2, 256, FAKE, FAKE, FAKE, None) == E_VALUE
+    assert f(FAKE, FAKE, None, float("nan"), 2, 256, FAKE, FAKE, FAKE, None) == E_VALUE
+    assert f(None, FAKE, None, 1e-5, 2, 256, FAKE, FAKE, FAKE, None) == E_NULL
+    assert f(FAKE, FAKE, None, 1e-5, 2, 256, FAKE, None, FAKE, None) == E_NULL
+    assert f(MIS, FAKE, None, 1e-5, 2, 256, FAKE, FAKE, FAKE, None) == E_ALIGN
+    assert f(FAKE, FAKE, FAKE + 4, 1e-5, 2, 256, FAKE, FAKE, FAKE, None) == E_ALIGN
+    assert f(FAKE, FAKE, None, 1e-5, 2, 256, MIS, FAKE, FAKE, None) == E_ALIGN
+    assert "bitnet_ffn_act_quant_i8" in _err(L)
+    assert f(None, None, None, 1e-5, 0, 256, None, None, None, None) == OK
 
 
 def test_last_error_is_per_thread(L):

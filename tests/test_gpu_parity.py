@@ -557,3 +557,70 @@ def test_gemv_group(bn, Ms, K, N):
         D, _ = oracle.linear_i2s(Pr, K, q, s, alpha, nthreads=8, want_y=False)
         np.testing.assert_array_equal(d.cpu().numpy(), D)
         check_y(y.cpu().numpy(), D, alpha, s)
+
+
+# ------------------------------------- squared-ReLU gated FFN activation
+def check_ffn_act(bn, g, u, gamma, eps):
+    q, s, qs, _ = oracle.ffn_act_quant(g, u, gamma, eps)
+    xq, xs, xsum = bn.ffn_act_quant(dev(g), dev(u), None if gamma is None else dev(gamma), eps)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(xsum.cpu().numpy(), qs)
+
+
+@pytest.mark.parametrize("N,F", [(1, 128), (5, 2048), (1, 6912), (64, 6912), (2, 32768)])
+@pytest.mark.parametrize("eps,with_gamma", [(1e-5, True), (1e-6, False)])
+def test_ffn_act_quant(bn, N, F, eps, with_gamma):
+    """Bit for bit with the oracle: codes, scales and sums."""
+    rng = np.random.default_rng(N * 7 + F)
+    g = (rng.standard_normal((N, F)) * 0.5).astype(np.float32)
+    u = (rng.standard_normal((N, F)) * 0.5).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, F).astype(np.float32) if with_gamma else None
+    check_ffn_act(bn, g, u, gamma, eps)
+
+
+def test_ffn_act_quant_edges(bn):
+    """All gates non-positive (the token normalises to zero), a single live
+    channel, constant rows, and huge/tiny magnitudes."""
+    F = 256
+    g = np.zeros((6, F), np.float32)
+    u = np.ones((6, F), np.float32)
+    g[0] = -1.0
+    g[1, 77] = 3.0
+    g[2] = 0.75
+    g[3] = np.linspace(-1e3, 1e3, F, dtype=np.float32)
+    g[4] = np.linspace(-1e-6, 1e-6, F, dtype=np.float32)
+    g[5, ::2] = 1.0
+    u[5, ::4] = -2.0
+    check_ffn_act(bn, g, u, None, 1e-5)
+
+
+@pytest.mark.parametrize("N", [1, 4, 128])
+def test_ffn_block_2b(bn, N):
+    """The 2B-class FFN block through the library (gate/up -> activation ->
+    down): the GPU activation codes equal the oracle's on the GPU's own gate
+    and up outputs, and down's int32 dots equal the oracle's on those codes."""
+    rng = np.random.default_rng(300 + N)
+    F, H = synth.SHAPES["b2"]["gate"]
+    Wg, Wu = synth.ternary(rng, F, H), synth.ternary(rng, F, H)
+    Wd = synth.ternary(rng, H, F)
+    ag, au, ad = (synth.weight_scale(rng) for _ in range(3))
+    gamma = rng.uniform(0.5, 1.5, F).astype(np.float32)
+    x = synth.tokens_bf16(rng, N, H)
+    Pg, Pu, Pd = bn.pack(dev(Wg)), bn.pack(dev(Wu)), bn.pack(dev(Wd))
+    outs, _ = bn.linear(to_bf16_tensor(x), [(Pg, ag), (Pu, au)])
+    (_, gy), (_, uy) = outs
+    xq, xs, xsum = bn.ffn_act_quant(gy, uy, dev(gamma), 1e-5)
+    d, y = bn.ffn(to_bf16_tensor(x), (Pg, ag), (Pu, au), (Pd, ad), dev(gamma), 1e-5)
+    torch.cuda.synchronize()
+    q, s, qs, _ = oracle.ffn_act_quant(gy.cpu().numpy(), uy.cpu().numpy(), gamma, 1e-5)
+    np.testing.assert_array_equal(xq.cpu().numpy(), q)
+    np.testing.assert_array_equal(xs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    Pd_ref, _ = oracle.pack_i2s(Wd)
+    rows = [(0, H)] if N < 128 else [(0, 64), (H - 64, 64)]
+    for r0, nr in rows:
+        D, _ = oracle.linear_i2s(oracle.pack_i2s(Wd[r0:r0 + nr])[0], F, q, s, ad, nthreads=8,
+                                 want_y=False)
+        np.testing.assert_array_equal(d.cpu().numpy()[:, r0:r0 + nr], D)
+        check_y(y.cpu().numpy()[:, r0:r0 + nr], D, ad, s)
