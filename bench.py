@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "1c43d5733cf67cf90848d094f05f8b232939b8626edf9f91a6f1e6c42385ac12",
+           "sha256": "182fb0491962b312d163205e782fbad57b699f280222773f780dcde85045c6bc",
            "bytes_per_launch": 4578816}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
