@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.orc_dot_def.restype = None
         L.orc_dot_raw.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
         L.orc_dot_raw.restype = None
+        L.orc_lut_tables.argtypes = [_p, _i64, _p]
+        L.orc_lut_tables.restype = None
+        L.orc_dot_lut.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.orc_dot_lut.restype = None
         L.orc_epilogue.argtypes = [_p, ctypes.c_double, _p, _i64, _i64, _p]
         L.orc_epilogue.restype = None
         L.orc_linear_i2s.argtypes = [_p, _i64, _i64, _p, _i64, _p, ctypes.c_float,
@@ -172,6 +176,31 @@ def dot_raw(packed: np.ndarray, q: np.ndarray, qsum: np.ndarray, K: int):
     R = np.zeros((N, M), dtype=np.int64)
     D = np.zeros((N, M), dtype=np.int64)
     lib().orc_dot_raw(_ptr(packed), _ptr(q), _ptr(qsum), M, K, N, _ptr(R), _ptr(D))
+    return R, D
+
+
+def lut_tables(q: np.ndarray, K: int) -> np.ndarray:
+    """[P1 §4-4, §11-2] per-group lookup tables of one token: int32 [K/2][16],
+    entry 4*c_hi + c_lo = c_hi*x_first + c_lo*x_second over raw codes 0..3."""
+    q = np.ascontiguousarray(q, dtype=np.int8).reshape(K)
+    t = np.zeros((K // 2, 16), dtype=np.int32)
+    lib().orc_lut_tables(_ptr(q), K, _ptr(t))
+    return t
+
+
+def dot_lut(packed: np.ndarray, q: np.ndarray, qsum: np.ndarray, K: int):
+    """[P1 §4-3, §4-4] raw-code dot by table lookup (tables first, then one
+    lookup per nibble); returns (R, D) like dot_raw."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1, K // 4)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    if q.ndim == 1:
+        q = q[None, :]
+    qsum = np.ascontiguousarray(qsum, dtype=np.int32)
+    M = packed.shape[0]
+    N = q.shape[0]
+    R = np.zeros((N, M), dtype=np.int64)
+    D = np.zeros((N, M), dtype=np.int64)
+    lib().orc_dot_lut(_ptr(packed), _ptr(q), _ptr(qsum), M, K, N, _ptr(R), _ptr(D))
     return R, D
 
 

@@ -182,6 +182,51 @@ void orc_dot_raw(const uint8_t *packed, const int8_t *q, const int32_t *qsum,
     }
 }
 
+/* ---- lookup-table route ------------------------------------------------ */
+
+void orc_lut_tables(const int8_t *q, int64_t K, int32_t *table)
+{
+    /* Phase one of the LUT method [P1 §4-4]: every value a group of two
+     * raw codes can contribute is tabulated from the activations alone. */
+    for (int64_t t = 0; t < K / 4; t++) {
+        int64_t base = (t / 32) * ORC_QK + (t % 32);
+        for (int half = 0; half < 2; half++) {
+            int64_t first = base + 64 * half;   /* fields 0,1 or fields 2,3 */
+            int32_t xa = q[first], xb = q[first + 32];
+            int32_t *entry = table + (2 * t + half) * 16;
+            for (int c_hi = 0; c_hi < 4; c_hi++)
+                for (int c_lo = 0; c_lo < 4; c_lo++)
+                    entry[4 * c_hi + c_lo] = c_hi * xa + c_lo * xb;
+        }
+    }
+}
+
+void orc_dot_lut(const uint8_t *packed, const int8_t *q, const int32_t *qsum,
+                 int64_t M, int64_t K, int64_t N, int64_t *R, int64_t *D)
+{
+    /* Phase two [P1 §4-4]: only after the whole table exists, each packed
+     * byte is split into its two nibbles and each nibble indexes its group's
+     * table; the lookups add up to the raw-code sum R, corrected as in the
+     * unpack route. */
+    int64_t bytes_per_row = K / 4;
+    int32_t *table = (int32_t *)malloc((size_t)(K / 2) * 16 * sizeof(int32_t));
+    if (!table) abort();
+    for (int64_t n = 0; n < N; n++) {
+        orc_lut_tables(q + n * K, K, table);
+        for (int64_t m = 0; m < M; m++) {
+            const uint8_t *rowbytes = packed + m * bytes_per_row;
+            int64_t raw = 0;
+            for (int64_t t = 0; t < bytes_per_row; t++) {
+                raw += table[(2 * t) * 16 + (rowbytes[t] >> 4)];
+                raw += table[(2 * t + 1) * 16 + (rowbytes[t] & 15)];
+            }
+            R[n * M + m] = raw;
+            D[n * M + m] = raw - (int64_t)qsum[n];
+        }
+    }
+    free(table);
+}
+
 void orc_epilogue(const int64_t *D, double alpha, const float *s, int64_t M,
                   int64_t N, double *y)
 {

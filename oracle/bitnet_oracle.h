@@ -72,6 +72,22 @@ void orc_dot_def(const int8_t *w, const int8_t *q, int64_t M, int64_t K,
 void orc_dot_raw(const uint8_t *packed, const int8_t *q, const int32_t *qsum,
                  int64_t M, int64_t K, int64_t N, int64_t *R, int64_t *D);
 
+/* Lookup-table route to the same raw-code dot [P1 §4-3 (the LUT path's entry
+ * condition), §4-4 (its order: the table is built from the activations
+ * before any lookup, with a barrier between the two phases); P1 §11-2
+ * (T-MAC, the lookup-based low-bit method it follows)].  A weight group is the two
+ * 2-bit fields of one nibble of an I2_S byte: the high nibble of byte t pairs
+ * the activations at (block start + t mod 32) and 32 places after, the low
+ * nibble those 64 and 96 places after.  Group g = 2t (high) or 2t + 1 (low)
+ * of a row of K weights; there are K/2 groups.
+ * orc_lut_tables: for one token q[K], table[g][c] (16 entries per group,
+ * c = 4*c_hi + c_lo over raw codes 0..3) = c_hi * x_first + c_lo * x_second.
+ * orc_dot_lut: per token, build the tables, then R[n][m] = sum over the
+ * row's nibbles of table[g][nibble]; D = R - qsum[n] as in orc_dot_raw. */
+void orc_lut_tables(const int8_t *q, int64_t K, int32_t *table);
+void orc_dot_lut(const uint8_t *packed, const int8_t *q, const int32_t *qsum,
+                 int64_t M, int64_t K, int64_t N, int64_t *R, int64_t *D);
+
 /* Dequantising epilogue [P2 §3 (scale left to the caller); P1 §4-5; P4]:
  * y[n][m] = D[n][m] * alpha / s[n], in double. */
 void orc_epilogue(const int64_t *D, double alpha, const float *s,

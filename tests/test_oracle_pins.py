@@ -225,6 +225,89 @@ def test_closed_forms(orc):
     np.testing.assert_array_equal(D[0], D[1])
 
 
+# ------------------------------------------------------- lookup-table route
+@pytest.mark.parametrize("M,K,N", [(5, 128, 1), (16, 384, 3), (7, 1280, 2)])
+def test_lut_dot_equals_definition(orc, M, K, N):
+    # The table route must reach the definition's integers exactly.
+    rng = np.random.default_rng(7 * M + K + N)
+    for dist in ("uniform", "half_zero"):
+        W = synth.ternary(rng, M, K, dist)
+        q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+        qsum = q.astype(np.int64).sum(1).astype(np.int32)
+        P, _ = orc.pack_i2s(W)
+        R, D = orc.dot_lut(P, q, qsum, K)
+        Dd = orc.dot_def(W, q)
+        np.testing.assert_array_equal(D, Dd)
+        np.testing.assert_array_equal(R, Dd + qsum[:, None])
+
+
+def test_lut_one_hot_token_reads_each_code(orc):
+    # A one-hot token x = v*e_k makes R[m] = code(W[m][k]) * v: every position
+    # of a block must reach its own weight through its group and nibble half
+    # (a swapped pair, a swapped nibble or a transposed table index fails).
+    rng = np.random.default_rng(123)
+    M, K = 6, 256
+    W = synth.ternary(rng, M, K)
+    P, _ = orc.pack_i2s(W)
+    for k in range(K):
+        for v in (1, -7):
+            e = np.zeros((1, K), dtype=np.int8)
+            e[0, k] = v
+            R, D = orc.dot_lut(P, e, np.array([v], dtype=np.int32), K)
+            np.testing.assert_array_equal(R[0], (W[:, k].astype(np.int64) + 1) * v)
+            np.testing.assert_array_equal(D[0], W[:, k].astype(np.int64) * v)
+
+
+def test_lut_tables_closed_forms(orc):
+    rng = np.random.default_rng(321)
+    K = 384
+    q = rng.integers(-128, 128, size=K, dtype=np.int8)
+    T = orc.lut_tables(q, K).astype(np.int64)
+    assert T.shape == (K // 2, 16)
+    # both codes 0 contribute nothing
+    assert (T[:, 0] == 0).all()
+    # every activation sits in exactly one group: the all-zero-weight entries
+    # (codes 1,1) add up to the token sum, and so do the lone-first plus
+    # lone-second entries (codes 1,0 and 0,1)
+    assert T[:, 5].sum() == q.astype(np.int64).sum()
+    assert T[:, 4].sum() + T[:, 1].sum() == q.astype(np.int64).sum()
+    # each table is bilinear in the two codes: entry(a,b) = a*entry(1,0) + b*entry(0,1)
+    for a in range(4):
+        for b in range(4):
+            np.testing.assert_array_equal(T[:, 4 * a + b], a * T[:, 4] + b * T[:, 1])
+    # the first activation of the high-nibble group of byte t is the one at
+    # block start + t mod 32 (one-hot probes)
+    for k in (0, 5, 31, 32, 63, 64, 96, 127, 128, 200, 383):
+        e = np.zeros(K, dtype=np.int8)
+        e[k] = 3
+        Te = orc.lut_tables(e, K)
+        nz = np.nonzero(Te[:, 4] + Te[:, 1])[0]
+        blk, p = divmod(k, 128)
+        t = blk * 32 + p % 32
+        g = 2 * t + (1 if p >= 64 else 0)
+        assert list(nz) == [g]
+        first = (p % 64) < 32
+        assert Te[g, 4] == (3 if first else 0) and Te[g, 1] == (0 if first else 3)
+
+
+def test_lut_counts_code3_like_the_raw_dot(orc):
+    # Any nibble is a valid table index: a code-3 slot contributes 3*x, as in
+    # the raw-code walk (both routes give the same R on arbitrary bytes).
+    rng = np.random.default_rng(77)
+    M, K, N = 9, 512, 2
+    P = rng.integers(0, 256, size=(M, K // 4), dtype=np.uint8)
+    q = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    qsum = q.astype(np.int64).sum(1).astype(np.int32)
+    R1, D1 = orc.dot_lut(P, q, qsum, K)
+    R2, D2 = orc.dot_raw(P, q, qsum, K)
+    np.testing.assert_array_equal(R1, R2)
+    np.testing.assert_array_equal(D1, D2)
+    # all bytes 0xFF: every weight has code 3, so R = 3 * sum(x)
+    P3 = np.full((1, K // 4), 0xFF, dtype=np.uint8)
+    R3, _ = orc.dot_lut(P3, q, qsum, K)
+    np.testing.assert_array_equal(R3[:, 0], 3 * q.astype(np.int64).sum(1))
+
+
 # ------------------------------------------------------- quantisation
 def test_quant_absmax_maps_to_127(orc):
     rng = np.random.default_rng(5)
