@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the secondary per-row measurements")
     ap.add_argument("--only", choices=("pack", "convert", "quant", "decode", "large", "prefill",
-                                       "ffn"),
+                                       "ffn", "lut"),
                     help="run only this group of secondary rows and print them (profiling aid)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times "
@@ -227,7 +227,7 @@ def secondary_rows(bn, synth, torch, stack, only=None):
     rows = {}
     parts = {"pack": row_pack, "convert": row_convert, "quant": row_quant,
              "decode": row_decode, "large": row_large, "prefill": row_prefill,
-             "ffn": row_ffn}
+             "ffn": row_ffn, "lut": row_lut}
     for name, fn in parts.items():
         if only is None or only == name:
             rows.update(fn(bn, synth, torch, stack))
@@ -370,6 +370,49 @@ def row_decode(bn, synth, torch, stack):
     return rows
 
 
+def row_lut(bn, synth, torch, stack):
+    """NEXT f4: the table-lookup decode matmul against the unpack GEMV on the
+    same launches (one per matrix, int8 tokens, N = 1, weights from HBM): the
+    2B-class stack (30 layers x 7 matrices) and eight 28672x8192 matrices of
+    the large layer's gate shape (470 MB packed)."""
+    rows = {}
+    cases = []
+    bufs = []
+    for layer in stack:
+        for xg, xq, xs, xsum, mats in layer["groups"]:
+            K = xg.shape[1]
+            q = bn.quant_act(synth.tokens_bf16_torch(1, K, 19 + K))
+            for P, alpha, dot, y, M, _ in mats:
+                bufs.append((P, alpha, q, dot, y, M, K))
+    cases.append(("b2", "2B-class stack, 30 layers x 7 matrices, one launch each", bufs))
+    M, K = synth.SHAPES["large"]["gate"]
+    big = []
+    q = bn.quant_act(synth.tokens_bf16_torch(1, K, 23))
+    for l in range(8):
+        W = synth.ternary_torch(M, K, synth.stack_seed("large", l, "gate", "weights"))
+        P = bn.pack(W)
+        del W
+        big.append((P, 0.02, q, torch.empty((1, M), dtype=torch.int32, device="cuda"),
+                    torch.empty((1, M), dtype=torch.float32, device="cuda"), M, K))
+    cases.append(("large_gate", "8 x 28672x8192 matrices, one launch each", big))
+    for tag, what, bufs in cases:
+        byts = sum(M * K // 4 + K + M * 8 for P, a, q, d, yy, M, K in bufs)
+        for how in ("lut", "unpack"):
+            fn = bn.gemv_lut if how == "lut" else bn.gemv
+
+            def run(bufs=bufs, fn=fn):
+                for P, alpha, q, d, yy, M, K in bufs:
+                    fn(P, alpha, q[0], q[1], q[2], out=(d, yy))
+            g = capture(torch, run)
+            t = time_graph(torch, g, 10, 3) / 10
+            del g
+            rows[f"lut_{tag}_N1_{how}"] = {"workload": what, "us_per_step": round(t * 1e6, 1),
+                                           "us_per_launch": round(t * 1e6 / len(bufs), 2),
+                                           "GB/s": round(byts / t / 1e9, 1),
+                                           "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del big
+    return rows
+
 def row_large(bn, synth, torch, stack):
     """a3 at streaming sizes: the large-layer stack (8 layers x 7 projections,
     1.71 GB packed, streamed from HBM every step).  N = 1: one grouped GEMV
@@ -503,7 +546,7 @@ def main():
 
     if args.only:
         # one group of secondary rows alone (for profiling); not the bench line
-        stack = build_stack(bn, synth, torch, args.layers) if args.only == "decode" else None
+        stack = build_stack(bn, synth, torch, args.layers) if args.only in ("decode", "lut") else None
         rows = secondary_rows(bn, synth, torch, stack, only=args.only)
         print(json.dumps({"only": args.only, "rows": rows}), flush=True)
         return

@@ -46,6 +46,7 @@ extern "C" {
 #define BITNET_GEMV_MAX_N 64        /* largest token count of the decode call */
 #define BITNET_GEMM_MAX_N (1 << 21) /* largest token count of the prefill call */
 #define BITNET_MAX_GROUP 8          /* matrices per bitnet_linear_i2s call     */
+#define BITNET_LUT_MAX_K 8192       /* largest K of the table-lookup decode call */
 
 typedef enum {
     BITNET_OK = 0,
@@ -126,6 +127,25 @@ int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t M,
                        int64_t K, const int8_t *xq, const float *x_scale,
                        const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
                        void *stream);
+
+/*
+ * bitnet_gemv_i2s_lut -- the decode matmul of bitnet_gemv_i2s_i8 computed by
+ * table lookup instead of unpacking the codes [P1 §4-3, §4-4 (the LUT route:
+ * tables are built from the activations alone, then, after a barrier, the
+ * weights index them); P1 §11-2 (T-MAC)].  For each token the call tabulates,
+ * for every pair of 2-bit fields sharing a nibble of an I2_S byte, the 16
+ * raw-code sums c_hi * x_first + c_lo * x_second, then sums one table entry
+ * per nibble of each row; D = that sum minus x_sum[n].
+ *
+ * Arguments, layouts, outputs and errors are those of bitnet_gemv_i2s_i8
+ * (identical dot and y, bit for bit), plus BITNET_E_SHAPE for
+ * K > BITNET_LUT_MAX_K (the tables of a token live in 16*K bytes of LDS).
+ * Weights are read once per token (no reuse across tokens): meant for N = 1.
+ */
+int bitnet_gemv_i2s_lut(const uint8_t *packed, float w_scale, int64_t M,
+                        int64_t K, const int8_t *xq, const float *x_scale,
+                        const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
+                        void *stream);
 
 /*
  * bitnet_linear_i2s -- fused decode linear: quantise tokens and multiply them

@@ -57,6 +57,7 @@ def load() -> ctypes.CDLL:
     sig = [p, f32, i64, i64, p, p, p, i64, p, p, p]
     L.bitnet_gemv_i2s_i8.argtypes = sig
     L.bitnet_gemm_i2s_i8.argtypes = sig
+    L.bitnet_gemv_i2s_lut.argtypes = sig
     L.bitnet_linear_i2s.argtypes = [p, ctypes.c_int, i64, i64, ctypes.POINTER(I2SMatrix),
                                     ctypes.c_int, p, p, p, p]
     L.bitnet_linear_i2s.restype = ctypes.c_int
@@ -72,7 +73,7 @@ def load() -> ctypes.CDLL:
     L.bitnet_pack_i2s_f32.argtypes = [p, i64, i64, p, ctypes.POINTER(ctypes.c_float), p]
     L.bitnet_pack_i2s_f32.restype = ctypes.c_int
     for fn in ("bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
-               "bitnet_gemm_i2s_i8", "bitnet_abi_version"):
+               "bitnet_gemm_i2s_i8", "bitnet_gemv_i2s_lut", "bitnet_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.bitnet_abi_version.argtypes = []
     L.bitnet_last_error.argtypes = []
@@ -188,6 +189,14 @@ def gemv(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=No
     """Decode matmul (1..64 tokens) -> (int32 dot[N][M] | None, fp32 y[N][M] | None)."""
     K = xq.shape[1]
     return _matmul(load().bitnet_gemv_i2s_i8, packed, w_scale, K, xq, x_scale,
+                   x_sum, want_dot, want_y, out)
+
+
+def gemv_lut(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
+    """Decode matmul by table lookup (K <= 8192) -> (dot | None, y | None),
+    the same values as gemv."""
+    K = xq.shape[1]
+    return _matmul(load().bitnet_gemv_i2s_lut, packed, w_scale, K, xq, x_scale,
                    x_sum, want_dot, want_y, out)
 
 

@@ -255,6 +255,22 @@ BITNET_API int bitnet_gemv_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
     return ok();
 }
 
+BITNET_API int bitnet_gemv_i2s_lut(const uint8_t *packed, float w_scale, int64_t M, int64_t K,
+                                   const int8_t *xq, const float *x_scale,
+                                   const int32_t *x_sum, int64_t N, int32_t *dot, float *y,
+                                   void *stream) {
+    const char *fn = "bitnet_gemv_i2s_lut";
+    if (int s = check_matmul(fn, packed, M, K, xq, x_scale, x_sum, N, BITNET_GEMV_MAX_N, dot, y))
+        return s;
+    if (K > BITNET_LUT_MAX_K)
+        return fail(BITNET_E_SHAPE, "%s: K=%lld exceeds %d", fn, (long long)K, BITNET_LUT_MAX_K);
+    if (M == 0 || N == 0) return ok();
+    hipError_t e = bitnet::launch_gemv_lut(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot, y,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("bitnet_gemv_i2s_lut: launch", e);
+    return ok();
+}
+
 BITNET_API int bitnet_gemm_i2s_i8(const uint8_t *packed, float w_scale, int64_t M, int64_t K,
                                   const int8_t *xq, const float *x_scale,
                                   const int32_t *x_sum, int64_t N, int32_t *dot, float *y,

@@ -150,6 +150,11 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
 hipError_t launch_gemv_mfma(const uint8_t *packed, float alpha, int64_t M, int64_t K,
                             const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
                             int32_t *dot, float *y, hipStream_t st);
+// Decode matmul by table lookup (per-token nibble-group tables in LDS, then
+// lookups); 1 <= N, K <= 8192 (the tables take 16*K bytes of LDS).
+hipError_t launch_gemv_lut(const uint8_t *packed, float alpha, int64_t M, int64_t K,
+                           const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
+                           int32_t *dot, float *y, hipStream_t st);
 // Prefill launch over up to kMaxMats matrices that share K and the tokens;
 // output tiles [tile_begin, next tile_begin) belong to matrix i.
 struct GemmMat {

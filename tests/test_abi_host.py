@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     fns = set(declared_functions())
     assert {"bitnet_pack_i2s", "bitnet_quant_act_i8", "bitnet_gemv_i2s_i8",
             "bitnet_gemm_i2s_i8", "bitnet_gemm_i2s_i8_group", "bitnet_gemv_i2s_i8_group",
-            "bitnet_linear_i2s",
+            "bitnet_linear_i2s", "bitnet_gemv_i2s_lut",
             "bitnet_absmean_i2s", "bitnet_pack_i2s_f32", "bitnet_ffn_act_quant_i8",
             "bitnet_last_error",
             "bitnet_abi_version"} <= fns
@@ -84,7 +84,8 @@ def test_quant_validation(L):
 
 
 @pytest.mark.parametrize("name,maxn", [("bitnet_gemv_i2s_i8", 64),
-                                       ("bitnet_gemm_i2s_i8", 1 << 21)])
+                                       ("bitnet_gemm_i2s_i8", 1 << 21),
+                                       ("bitnet_gemv_i2s_lut", 64)])
 def test_matmul_validation(L, name, maxn):
     f = getattr(L, name)
     a = dict(packed=FAKE, s=0.05, M=16, K=256, xq=FAKE, xs=FAKE, xsum=FAKE, N=1,
@@ -113,6 +114,11 @@ def test_matmul_validation(L, name, maxn):
     assert call(M=0, packed=None, xq=None) == OK
     assert call(N=0, packed=None, xq=None) == OK
     assert _err(L) == ""
+    if name == "bitnet_gemv_i2s_lut":
+        # the tables of one token take 16*K bytes of LDS: K <= 8192
+        assert call(K=8192 + 128) == E_SHAPE
+        assert "8192" in _err(L)
+        assert call(K=8192 + 128, M=0) == E_SHAPE
 
 
 def test_linear_validation(L):

@@ -49,7 +49,7 @@ def check_y(y, D, alpha, s):
 
 
 def gpu_linear(bn, P_gpu, alpha, xq, xs, xsum, entry):
-    fn = bn.gemv if entry == "gemv" else bn.gemm
+    fn = {"gemv": bn.gemv, "gemm": bn.gemm, "lut": bn.gemv_lut}[entry]
     dot, y = fn(P_gpu, alpha, xq, xs, xsum)
     torch.cuda.synchronize()
     return dot.cpu().numpy(), y.cpu().numpy()
@@ -624,3 +624,77 @@ def test_ffn_block_2b(bn, N):
                                  want_y=False)
         np.testing.assert_array_equal(d.cpu().numpy()[:, r0:r0 + nr], D)
         check_y(y.cpu().numpy()[:, r0:r0 + nr], D, ad, s)
+
+
+# ------------------------------------------------------ lookup-table decode
+LUT_SMALL = [(1, 128, 1), (5, 128, 2), (17, 384, 3), (64, 256, 1), (65, 640, 1),
+             (100, 1280, 4), (129, 2048, 1), (300, 2560, 2), (70, 8192, 1), (33, 6912, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", LUT_SMALL)
+def test_gemv_lut_small(bn, M, K, N):
+    """Tables + lookups on the GPU vs the oracle: int32 dot bit for bit, y to
+    the epilogue tolerance (ragged row tiles, 1..16 waves, K up to 8192)."""
+    run_case(bn, M, K, N, "lut", seed=M * 7 + K + N)
+
+
+@pytest.mark.parametrize("proj", synth.PROJ_NAMES)
+def test_gemv_lut_b2_decode_shapes(bn, proj):
+    M, K = synth.SHAPES["b2"][proj]
+    run_case(bn, M, K, 1, "lut", seed=40 + synth.PROJ_NAMES.index(proj))
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "gate"])
+def test_gemv_lut_large_sampled(bn, proj):
+    M, K = synth.SHAPES["large"][proj]
+    rows = [(0, 48), (M // 2 + 5, 48), (M - 33, 33)]
+    run_case(bn, M, K, 1, "lut", seed=200 + len(proj), rows=rows)
+
+
+def test_gemv_lut_equals_unpack_bitwise(bn):
+    """Arbitrary packed bytes (code 3 included): the lookup route, the unpack
+    GEMV and the oracle's raw-code walk give the same D, and the two kernels
+    the same y bits."""
+    rng = np.random.default_rng(11)
+    M, K, N = 257, 2560, 3
+    P = rng.integers(0, 256, size=(M, K // 4), dtype=np.uint8)
+    x = synth.tokens_bf16(rng, N, K)
+    xq, xs, xsum = bn.quant_act(to_bf16_tensor(x))
+    Pg = dev(P)
+    d1, y1 = bn.gemv_lut(Pg, 0.013, xq, xs, xsum)
+    d2, y2 = bn.gemv(Pg, 0.013, xq, xs, xsum)
+    torch.cuda.synchronize()
+    q, s, qs = oracle.quant_act(x)
+    _, D = oracle.dot_raw(P, q, qs, K)
+    np.testing.assert_array_equal(d1.cpu().numpy(), D)
+    np.testing.assert_array_equal(d2.cpu().numpy(), D)
+    np.testing.assert_array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+
+
+def test_gemv_lut_edges(bn):
+    """All -1 / 0 / +1 rows, every activation at +-127 at the largest K, the
+    optional outputs, and the zero sizes."""
+    K, N = 8192, 2
+    W = np.zeros((3 * 40, K), dtype=np.int8)
+    W[:40] = -1
+    W[80:] = 1
+    x = np.full((N, K), 3.0, dtype=np.float32)
+    x[1, ::2] = -3.0
+    P = bn.pack(dev(W))
+    xq, xs, xsum = bn.quant_act(dev(x))
+    dot, y = bn.gemv_lut(P, 0.07, xq, xs, xsum)
+    d_only, none_y = bn.gemv_lut(P, 0.07, xq, xs, xsum, want_y=False)
+    none_d, y_only = bn.gemv_lut(P, 0.07, xq, xs, xsum, want_dot=False)
+    torch.cuda.synchronize()
+    d = dot.cpu().numpy()
+    qs = xsum.cpu().numpy()
+    assert qs[0] == 127 * K and qs[1] == 0
+    assert (d[:, :40] == -qs[:, None]).all()
+    assert (d[:, 40:80] == 0).all() and (y.cpu().numpy()[:, 40:80] == 0).all()
+    assert (d[:, 80:] == qs[:, None]).all()
+    assert none_y is None and none_d is None
+    assert torch.equal(d_only, dot) and torch.equal(y_only, y)
+    e = torch.empty((0, K), dtype=torch.int8, device="cuda")
+    bn.gemv_lut(P, 0.5, e, xs[:0], xsum[:0])
+    bn.gemv_lut(P[:0], 0.5, xq, xs, xsum)
+    torch.cuda.synchronize()
