@@ -341,7 +341,8 @@ def row_quant(bn, synth, torch, stack):
 
 def row_decode(bn, synth, torch, stack):
     rows = {}
-    # a4: batched decode on the 2B stack shapes, N = 4, 16, 64 (weights from HBM)
+    # a4: batched decode on the 2B stack shapes, N = 4, 16, 64 (weights from HBM):
+    # one launch per matrix, then one grouped launch per dependency group
     for N in (4, 16, 64):
         bufs = []
         for layer in stack:
@@ -367,6 +368,28 @@ def row_decode(bn, synth, torch, stack):
                                 "TOPS": round(ops / t / 1e12, 3),
                                 "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
         del bufs, g
+        groups = []
+        for layer in stack:
+            for xg, xq, xs, xsum, mats in layer["groups"]:
+                K = xg.shape[1]
+                q = bn.quant_act(synth.tokens_bf16_torch(N, K, 13 + N))
+                ms = [(P, alpha) for P, alpha, dot, y, M, _ in mats]
+                outs = [(torch.empty((N, M), dtype=torch.int32, device="cuda"),
+                         torch.empty((N, M), dtype=torch.float32, device="cuda"))
+                        for P, alpha, dot, y, M, _ in mats]
+                groups.append((ms, q, outs, K))
+
+        def run_g(groups=groups):
+            for ms, q, outs, K in groups:
+                bn.gemv_group(ms, q[0], q[1], q[2], out=outs)
+        g = capture(torch, run_g)
+        t = time_graph(torch, g, 10, 3) / 10
+        rows[f"decode_N{N}_grouped"] = {
+            "workload": "2B-class stack, 30 layers x 4 grouped launches (q/k/v, o, gate/up, down)",
+            "us_per_step": round(t * 1e6, 1), "GB/s": round(byts / t / 1e9, 1),
+            "TOPS": round(ops / t / 1e12, 3),
+            "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del groups, g
     return rows
 
 

@@ -164,7 +164,7 @@ int bitnet_gemv_i2s_lut(const uint8_t *packed, float w_scale, int64_t M,
  *              quantiser and the MFMA kernels).
  *
  * N <= 8: one launch quantises and multiplies.  8 < N <= BITNET_GEMV_MAX_N:
- * quantiser, then the batched-decode MFMA kernel per matrix.  Larger N
+ * quantiser, then one batched-decode MFMA launch for all matrices.  Larger N
  * (prefill): quantiser, then one grouped MFMA GEMM launch for all matrices.
  * Every output equals what bitnet_quant_act_i8 followed by
  * bitnet_gemv_i2s_i8 (N <= BITNET_GEMV_MAX_N) or bitnet_gemm_i2s_i8 on each
@@ -207,8 +207,8 @@ int bitnet_ffn_act_quant_i8(const float *g, const float *u, const float *gamma, 
 /*
  * bitnet_gemv_i2s_i8_group -- decode matmul (N <= BITNET_GEMV_MAX_N tokens,
  * already quantised) of several I2_S matrices that share the tokens: one
- * vector-ALU launch for all of them when N <= 2, else the batched-decode MFMA
- * kernel per matrix.  [P1 §2-1, §4-3; P2 §3; P3 §3.2]
+ * launch for all of them: the vector-ALU GEMV when N <= 2, else the
+ * batched-decode MFMA kernel.  [P1 §2-1, §4-3; P2 §3; P3 §3.2]
  *
  *   mats, xq, x_scale, x_sum   as bitnet_gemm_i2s_i8_group.
  *

@@ -249,7 +249,8 @@ BITNET_API int bitnet_gemv_i2s_i8(const uint8_t *packed, float w_scale, int64_t 
         e = bitnet::launch_gemv_valu(&m, 1, K, N, 0, xq, x_scale, x_sum, nullptr, nullptr,
                                      nullptr, st);
     } else {
-        e = bitnet::launch_gemv_mfma(packed, w_scale, M, K, xq, x_scale, x_sum, N, dot, y, st);
+        bitnet::GemmMat m{packed, dot, y, w_scale, (int)M, 0};
+        e = bitnet::launch_gemv_mfma(&m, 1, K, xq, x_scale, x_sum, N, st);
     }
     if (e != hipSuccess) return hip_fail("bitnet_gemv_i2s_i8: launch", e);
     return ok();
@@ -356,10 +357,11 @@ BITNET_API int bitnet_gemv_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mat
         e = bitnet::launch_gemv_valu(gm, n_mats, K, N, 0, xq, x_scale, x_sum, nullptr, nullptr,
                                      nullptr, st);
     } else {
-        for (int i = 0; i < n_mats && e == hipSuccess; ++i)
-            if (mats[i].M > 0)
-                e = bitnet::launch_gemv_mfma(mats[i].packed, mats[i].w_scale, mats[i].M, K, xq,
-                                             x_scale, x_sum, N, mats[i].dot, mats[i].y, st);
+        bitnet::GemmMat mm[bitnet::kMaxMats];
+        for (int i = 0; i < n_mats; ++i)
+            mm[i] = bitnet::GemmMat{mats[i].packed, mats[i].dot, mats[i].y, mats[i].w_scale,
+                                    (int)mats[i].M, 0};
+        e = bitnet::launch_gemv_mfma(mm, n_mats, K, xq, x_scale, x_sum, N, st);
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
@@ -420,10 +422,12 @@ static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int6
                                      nullptr, xq, x_scale, x_sum, st);
     } else if (N <= BITNET_GEMV_MAX_N) {
         e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
-        for (int i = 0; i < n_mats && e == hipSuccess; ++i)
-            if (gm[i].M > 0)
-                e = bitnet::launch_gemv_mfma(gm[i].packed, gm[i].alpha, gm[i].M, K, xq, x_scale,
-                                             x_sum, N, gm[i].dot, gm[i].y, st);
+        if (e == hipSuccess) {
+            bitnet::GemmMat mm[bitnet::kMaxMats];
+            for (int i = 0; i < n_mats; ++i)
+                mm[i] = bitnet::GemmMat{gm[i].packed, gm[i].dot, gm[i].y, gm[i].alpha, gm[i].M, 0};
+            e = bitnet::launch_gemv_mfma(mm, n_mats, K, xq, x_scale, x_sum, N, st);
+        }
     } else {
         e = bitnet::launch_quant(x, dtype == BITNET_BF16, N, K, xq, x_scale, x_sum, st);
         if (e == hipSuccess) {

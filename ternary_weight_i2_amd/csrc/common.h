@@ -146,10 +146,6 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
                             int mode, const void *x, const float *xs,
                             const int32_t *xsum, int8_t *xq_out, float *xs_out,
                             int32_t *xsum_out, hipStream_t st);
-// Batched decode (1..64 tokens) on MFMA, weights streamed once.
-hipError_t launch_gemv_mfma(const uint8_t *packed, float alpha, int64_t M, int64_t K,
-                            const int8_t *xq, const float *xs, const int32_t *xsum, int64_t N,
-                            int32_t *dot, float *y, hipStream_t st);
 // Decode matmul by table lookup (per-token nibble-group tables in LDS, then
 // lookups); 1 <= N, K <= 8192 (the tables take 16*K bytes of LDS).
 hipError_t launch_gemv_lut(const uint8_t *packed, float alpha, int64_t M, int64_t K,
@@ -174,6 +170,10 @@ struct GemmArgs {
     const float *xs;
     const int32_t *xsum;
 };
+// Batched decode (1..64 tokens) on MFMA, weights streamed once: every matrix
+// of `mats` (M > 0) times the same quantised tokens, in one launch.
+hipError_t launch_gemv_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
+                            const float *xs, const int32_t *xsum, int64_t N, hipStream_t st);
 // Prefill (any token count) on int8 MFMA: every matrix of `mats` (M > 0)
 // times the same quantised tokens, in one launch.
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,

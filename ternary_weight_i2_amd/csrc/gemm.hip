@@ -264,8 +264,11 @@ static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
     // Token tile matched to small N so no MFMA column work is wasted.
-    if (N <= 32) return run_gemm<128, 32, 4, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-    if (N <= 64) return run_gemm<128, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    // Token counts of batched decode: small row tiles, so that a launch over
+    // a 2B-class layer's matrices still spreads over the CUs (128-row tiles
+    // gave 108 workgroups for the gate/up pair and measured 20-25% slower).
+    if (N <= 32) return run_gemm<32, 32, 1, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    if (N <= 64) return run_gemm<64, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     // The K loop is bound by the LDS-DMA fills (removing its MFMAs leaves
     // three quarters of its time), so larger tiles -- more MFMA work per
     // staged byte -- win where there are enough of them: 256x128 tiles of

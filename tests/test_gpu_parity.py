@@ -154,7 +154,8 @@ def test_quant_edge_rows(bn):
 
 # ------------------------------------------------------ small-shape matmuls
 SMALL = [(1, 128, 1), (5, 128, 2), (17, 384, 3), (64, 256, 4), (100, 640, 5),
-         (129, 1152, 8), (33, 512, 9), (70, 896, 16), (130, 256, 31), (65, 384, 64)]
+         (129, 1152, 8), (33, 512, 9), (70, 896, 16), (50, 640, 24), (50, 640, 25),
+         (130, 256, 31), (97, 1280, 40), (65, 384, 64)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL)
@@ -533,7 +534,8 @@ def test_gemm_group_large_tiles_ragged(bn):
 
 
 @pytest.mark.parametrize("Ms,K,N", [((5, 0, 130), 128, 1), ((640, 640, 2560), 2560, 2),
-                                    ((257, 33), 384, 7), ((100, 200), 640, 64)])
+                                    ((257, 33), 384, 7), ((300, 41, 7), 1280, 24),
+                                    ((64, 0, 90), 512, 25), ((100, 200), 640, 64)])
 def test_gemv_group(bn, Ms, K, N):
     """Grouped decode GEMV vs bitnet_gemv_i2s_i8 per matrix (bit for bit) and
     the oracle."""
