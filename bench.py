@@ -305,7 +305,7 @@ def row_ffn(bn, synth, torch, stack):
 
         def run(bufs=bufs, N=N):
             for mats, gamma, gu, q, qx, out in bufs:
-                bn.linear(x, [mats["gate"], mats["up"]], out=gu, qout=qx if N > 8 else None)
+                bn.linear(x, [mats["gate"], mats["up"]], out=gu, qout=qx if N > 2 else None)
                 bn.ffn_act_quant(gu[0][1], gu[1][1], gamma, 1e-5, out=q)
                 P, a = mats["down"]
                 if N <= 64:
@@ -390,6 +390,31 @@ def row_decode(bn, synth, torch, stack):
             "TOPS": round(ops / t / 1e12, 3),
             "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
         del groups, g
+        # the same through bitnet_linear_i2s on bf16 tokens (the quantiser
+        # included: fused into the GEMV for N <= 2, its own launch above)
+        lin = []
+        for layer in stack:
+            for xg, xq, xs, xsum, mats in layer["groups"]:
+                K = xg.shape[1]
+                xb = synth.tokens_bf16_torch(N, K, 13 + N)
+                q = bn.quant_act(xb)
+                ms = [(P, alpha) for P, alpha, dot, y, M, _ in mats]
+                outs = [(torch.empty((N, M), dtype=torch.int32, device="cuda"),
+                         torch.empty((N, M), dtype=torch.float32, device="cuda"))
+                        for P, alpha, dot, y, M, _ in mats]
+                lin.append((xb, ms, outs, q))
+
+        def run_l(lin=lin):
+            for xb, ms, outs, q in lin:
+                bn.linear(xb, ms, out=outs, qout=q if N > 2 else None)
+        g = capture(torch, run_l)
+        t = time_graph(torch, g, 10, 3) / 10
+        lbytes = byts + sum(N * xb.shape[1] for xb, ms, outs, q in lin)   # bf16 tokens: one more byte each
+        rows[f"decode_N{N}_linear"] = {
+            "workload": "2B-class stack, bf16 tokens, bitnet_linear_i2s per dependency group",
+            "us_per_step": round(t * 1e6, 1), "GB/s": round(lbytes / t / 1e9, 1),
+            "hbm_frac": round(lbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del lin, g
     return rows
 
 
@@ -466,7 +491,7 @@ def row_large(bn, synth, torch, stack):
                 outs = [(torch.empty((N, P.shape[0]), dtype=torch.int32, device="cuda"),
                          torch.empty((N, P.shape[0]), dtype=torch.float32, device="cuda"))
                         for P, _ in mats]
-                qout = q if N > 8 else None
+                qout = q if N > 2 else None
                 bufs.append((x, q, mats, outs, qout))
 
         def run(bufs=bufs, how=how):
@@ -485,11 +510,11 @@ def row_large(bn, synth, torch, stack):
         M_out = sum(P.shape[0] for x, q, mats, outs, qout in bufs for P, _ in mats)
         tok_bytes = N * K_tok * (2 if how == "linear" else 1)
         byts = packed + tok_bytes + N * M_out * 8
-        tag = f"large_N{N}" + ("" if how == "group" or N > 8 else
+        tag = f"large_N{N}" + ("" if how == "group" or N > 2 else
                                {"linear": "_fused_bf16", "gemv": "_per_matrix"}[how])
         rows[tag] = {"workload": "large layer stack, 8 layers x 7 projections, 1.71 GB packed",
                      "launches": {"group": "32 grouped GEMV, int8 tokens",
-                                  "linear": ("32 fused quantise + GEMV, bf16 tokens" if N <= 8 else
+                                  "linear": ("32 fused quantise + GEMV, bf16 tokens" if N <= 2 else
                                              "32 x (quantiser + batched-decode GEMV), bf16 tokens"),
                                   "gemv": "56 GEMV, int8 tokens"}[how],
                      "us_per_step": round(t * 1e6, 1), "GB/s": round(byts / t / 1e9, 1),

@@ -46,6 +46,7 @@ extern "C" {
 #define BITNET_GEMV_MAX_N 64        /* largest token count of the decode call */
 #define BITNET_GEMM_MAX_N (1 << 21) /* largest token count of the prefill call */
 #define BITNET_MAX_GROUP 8          /* matrices per bitnet_linear_i2s call     */
+#define BITNET_LINEAR_FUSED_MAX_N 2 /* bitnet_linear_i2s: one fused launch up to this N */
 #define BITNET_LUT_MAX_K 8192       /* largest K of the table-lookup decode call */
 
 typedef enum {
@@ -158,12 +159,15 @@ int bitnet_gemv_i2s_lut(const uint8_t *packed, float w_scale, int64_t M,
  *              packed [M][K/4] I2_S (16-byte aligned), M, w_scale, and the
  *              outputs dot [N][M] int32 / y [N][M] fp32 (either may be NULL,
  *              not both, unless M == 0).
- *   xq, x_scale, x_sum   optional outputs (may be NULL when N <= 8): the
+ *   xq, x_scale, x_sum   optional outputs (may be NULL when
+ *              N <= BITNET_LINEAR_FUSED_MAX_N): the
  *              quantised tokens exactly as bitnet_quant_act_i8 writes them.
- *              Required when N > 8 (they then carry the tokens between the
+ *              Required for larger N (they then carry the tokens between the
  *              quantiser and the MFMA kernels).
  *
- * N <= 8: one launch quantises and multiplies.  8 < N <= BITNET_GEMV_MAX_N:
+ * N <= BITNET_LINEAR_FUSED_MAX_N: one launch quantises and multiplies (the
+ * vector-ALU GEMV; at more tokens it is ALU-bound and slower than the two
+ * launches below).  Up to BITNET_GEMV_MAX_N:
  * quantiser, then one batched-decode MFMA launch for all matrices.  Larger N
  * (prefill): quantiser, then one grouped MFMA GEMM launch for all matrices.
  * Every output equals what bitnet_quant_act_i8 followed by

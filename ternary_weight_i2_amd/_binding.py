@@ -16,6 +16,7 @@ _LIB_PATH = os.path.join(_HERE, "libbitnet_i2s.so")
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_VALUE, E_HIP = range(7)
 F32, BF16 = 0, 1
 GEMV_MAX_N = 64
+LINEAR_FUSED_MAX_N = 2     # bitnet_linear_i2s: one fused launch up to this N
 
 
 MAX_GROUP = 8
@@ -280,8 +281,8 @@ def ffn(x, gate, up, down, gamma=None, eps=1e-5):
 
 def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
     """Linear layer step: quantise tokens x[N][K] (fp32/bf16, cuda) and multiply
-    them by every (packed, w_scale) in ``mats`` -- one fused launch for N <= 8;
-    for N > 8 the library quantises into ``qout`` first (allocated here if
+    them by every (packed, w_scale) in ``mats`` -- one fused launch for N <= 2;
+    for N > 2 the library quantises into ``qout`` first (allocated here if
     None), then runs the batched-decode (N <= 64) or grouped prefill kernels.
 
     Returns ([(dot | None, y | None) per matrix], (xq, s, xsum) | None)."""
@@ -293,7 +294,7 @@ def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
         raise TypeError("x must be float32 or bfloat16")
     N, K = x.shape
     out = _mats_out(mats, N, x.device, want_dot, want_y, out)
-    if qout is None and N > 8:
+    if qout is None and N > LINEAR_FUSED_MAX_N:
         qout = (torch.empty((N, K), dtype=torch.int8, device=x.device),
                 torch.empty((N,), dtype=torch.float32, device=x.device),
                 torch.empty((N,), dtype=torch.int32, device=x.device))

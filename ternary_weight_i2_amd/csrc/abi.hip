@@ -413,11 +413,12 @@ static int linear_impl(const char *fn, const void *x, int dtype, int64_t N, int6
     if (!aligned(x, 16) || (xq && !aligned(xq, 16)) || (x_scale && !aligned(x_scale, 4)) ||
         (x_sum && !aligned(x_sum, 4)))
         return fail(BITNET_E_ALIGN, "%s: x/xq must be 16-byte and x_scale/x_sum 4-byte aligned", fn);
-    if (N > 8 && (!xq || !x_scale || !x_sum))
-        return fail(BITNET_E_NULL, "%s: N > 8 needs the xq, x_scale and x_sum buffers", fn);
+    if (N > BITNET_LINEAR_FUSED_MAX_N && (!xq || !x_scale || !x_sum))
+        return fail(BITNET_E_NULL, "%s: N > %d needs the xq, x_scale and x_sum buffers", fn,
+                    BITNET_LINEAR_FUSED_MAX_N);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (N <= 8) {
+    if (N <= BITNET_LINEAR_FUSED_MAX_N) {
         e = bitnet::launch_gemv_valu(gm, n_mats, K, N, dtype == BITNET_BF16 ? 2 : 1, x, nullptr,
                                      nullptr, xq, x_scale, x_sum, st);
     } else if (N <= BITNET_GEMV_MAX_N) {

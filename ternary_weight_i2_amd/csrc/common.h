@@ -140,7 +140,7 @@ hipError_t launch_pack(const int8_t *w, int64_t M, int64_t K, uint8_t *packed,
 hipError_t launch_quant(const void *x, int bf16, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t st);
 // Decode GEMV on the vector ALUs for any N (tokens are processed in passes of
-// at most 8).  mode 0: x is int8 xq with xs/xsum given; mode 1/2: x is fp32 /
+// at most 2).  mode 0: x is int8 xq with xs/xsum given; mode 1/2: x is fp32 /
 // bf16 and is quantised inside the kernel (xq_out/xs_out/xsum_out optional).
 hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N,
                             int mode, const void *x, const float *xs,

@@ -48,8 +48,7 @@ static GemvGeometry gemv_geometry(int64_t K, int64_t total_rows, int mode) {
     if (iters < 1) iters = 1;
     g.rows_per_wg = (int)(rows_per_iter * iters);
     g.per = (int)(kLdsBytes / K);
-    if (g.per > 8) g.per = 8;
-    if (mode == 0 && g.per > 2) g.per = 2;   // int8 tokens: passes of at most two
+    if (g.per > 2) g.per = 2;   // passes of at most two tokens (more run on MFMA)
     return g;
 }
 
@@ -94,13 +93,9 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
         if (nt == 1)
             e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, sr, g, st)
               : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, sr, g, st) : launch_gemv_nt<1, 2>(a, lpr, sr, g, st);
-        else if (nt == 2)
+        else
             e = mode == 0 ? launch_gemv_nt<2, 0>(a, lpr, sr, g, st)
               : mode == 1 ? launch_gemv_nt<2, 1>(a, lpr, sr, g, st) : launch_gemv_nt<2, 2>(a, lpr, sr, g, st);
-        else if (nt <= 4)
-            e = mode == 1 ? launch_gemv_nt<4, 1>(a, lpr, sr, g, st) : launch_gemv_nt<4, 2>(a, lpr, sr, g, st);
-        else
-            e = mode == 1 ? launch_gemv_nt<8, 1>(a, lpr, sr, g, st) : launch_gemv_nt<8, 2>(a, lpr, sr, g, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -468,11 +468,9 @@ hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, bool short_rows, unsigned 
 
 #define BITNET_GEMV_EXTERN(NT, MODE) \
     extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, bool, unsigned, hipStream_t)
-// int8 tokens (mode 0) take at most two per pass; the fused modes up to eight
+// passes of one or two tokens (larger batches run on MFMA)
 BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);
 BITNET_GEMV_EXTERN(2, 0); BITNET_GEMV_EXTERN(2, 1); BITNET_GEMV_EXTERN(2, 2);
-BITNET_GEMV_EXTERN(4, 1); BITNET_GEMV_EXTERN(4, 2);
-BITNET_GEMV_EXTERN(8, 1); BITNET_GEMV_EXTERN(8, 2);
 #undef BITNET_GEMV_EXTERN
 
 }  // namespace bitnet

@@ -151,7 +151,8 @@ def test_linear_validation(L):
              None, None, None, None) == E_SHAPE
     assert f(MIS, 1, 1, 256, g1, 1, None, None, None, None) == E_ALIGN
     assert f(FAKE, 1, 1, 256, g1, 1, MIS, None, None, None) == E_ALIGN
-    # N > 8 needs the token buffers
+    # N > BITNET_LINEAR_FUSED_MAX_N (2) needs the token buffers
+    assert f(FAKE, 1, 3, 256, g1, 1, None, None, None, None) == E_NULL
     assert f(FAKE, 1, 9, 256, g1, 1, None, None, None, None) == E_NULL
     # N == 0 and matrices with M == 0 are no-ops
     assert f(None, 1, 0, 256, g1, 1, None, None, None, None) == OK
@@ -275,3 +276,12 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "bitnet_oracle" not in text and "liboracle" not in text, fn
+
+
+def test_binding_limits_match_header():
+    from ternary_weight_i2_amd import _binding
+    text = open(HEADER).read()
+    for name, value in (("BITNET_GEMV_MAX_N", _binding.GEMV_MAX_N),
+                        ("BITNET_LINEAR_FUSED_MAX_N", _binding.LINEAR_FUSED_MAX_N)):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
