@@ -41,10 +41,11 @@ namespace bitnet {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN, int WM, int WN, int kStages>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs a) {
+template <int BM, int BN, int WM, int WN, int kStages, int KS>
+__global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const GemmArgs a) {
     static_assert(kStages >= 2, "at least double buffering");
-    constexpr int NW = WM * WN;        // waves per workgroup
+    static_assert(KS >= 1, "K groups");
+    constexpr int NW = WM * WN;        // waves per K group (one output tile)
     constexpr int MI = BM / WM / 32;   // 32-row MFMA tiles per wave
     constexpr int NJ = BN / WN / 32;   // 32-token MFMA tiles per wave
     static_assert(MI >= 1 && NJ >= 1, "tile too small");
@@ -58,10 +59,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     static_assert(CMIN >= 1, "every wave issues at least one DMA per block");
     constexpr int A_BYTES = BM * kBlockBytes, B_BYTES = BN * kBlock;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * STAGE];
+    // KS > 1 (launches too small to fill the CUs): KS groups of NW waves
+    // split K -- group g takes blocks g, g + KS, ... through its own stages --
+    // and their int32 partial sums meet in LDS at the end (exact).
+    constexpr int RED = KS > 1 ? (KS - 1) * NW * MI * NJ * 16 * 64 * 4 : 0;
+    static_assert(RED <= KS * kStages * STAGE, "partial sums reuse the staging memory");
+    __shared__ __attribute__((aligned(1024))) int8_t lds_all[KS * kStages * STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = (tid >> 6) % NW, grp = (tid >> 6) / NW;
+    int8_t *const lds = lds_all + grp * (kStages * STAGE);
     const int wm = wave % WM, wn = wave / WM;
     const int r32 = lane & 31, kg = lane >> 5;
     // Tile of this workgroup.  Workgroups are dealt to the XCDs round-robin
@@ -91,6 +98,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * BN;
     const int64_t rowb = K >> 2;
     const int nkb = K / kBlock;
+    const int nit = (nkb + KS - 1) / KS;   // iterations of every group (the last may idle)
 
     // Global source of this lane's 16 bytes in each of the wave's DMA
     // instructions (byte offset 1024*j of the stage; A first, then B).  Rows
@@ -152,12 +160,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     // re-fetched into a stage that is never read), so the wait below is a
     // constant: at most (kStages-2) newer blocks of DMA may still be pending.
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) issue(min(p, nkb - 1), p);
-    for (int kb = 0; kb < nkb; ++kb) {
+    for (int p = 0; p < kStages - 1; ++p) issue(min(p * KS + grp, nkb - 1), p);
+    for (int it = 0; it < nit; ++it) {
         wait_block();
-        __syncthreads();   // every wave's share of block kb is in LDS; stage (kb-1) is free
-        issue(min(kb + kStages - 1, nkb - 1), (kb + kStages - 1) % kStages);
-        const int8_t *sa = lds + (kb % kStages) * STAGE;
+        __syncthreads();   // every wave's share of this block is in LDS; stage (it-1) is free
+        issue(min((it + kStages - 1) * KS + grp, nkb - 1), (it + kStages - 1) % kStages);
+        if (KS > 1 && it * KS + grp >= nkb) continue;   // this group's share of K is done
+        const int8_t *sa = lds + (it % kStages) * STAGE;
         const int8_t *sb = sa + A_BYTES;
         // All of the block's fragments are read from LDS up front (one LDS
         // round trip), then the 4*MI*NJ MFMAs run back to back while the next
@@ -192,6 +201,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
         }
     }
     wait_vmcnt<0>();   // drain the trailing re-fetches before the workgroup ends
+    if constexpr (KS > 1) {
+        // groups 1..KS-1 hand their sums to group 0 through LDS, register by
+        // register (lane-contiguous, so no bank conflicts); group 0 adds them
+        // in group order and alone runs the epilogue.
+        __syncthreads();   // every group is done with its stages
+        int *red = reinterpret_cast<int *>(lds_all);
+        if (grp > 0) {
+            int *dst = red + (((grp - 1) * NW + wave) * MI * NJ * 16) * 64 + lane;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dst[((mi * NJ + nj) * 16 + e) * 64] = acc[mi][nj][e];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+        for (int g = 1; g < KS; ++g) {
+            const int *srcp = red + (((g - 1) * NW + wave) * MI * NJ * 16) * 64 + lane;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[mi][nj][e] += srcp[((mi * NJ + nj) * 16 + e) * 64];
+        }
+    }
 
     // 32x32 result layout: lane l, register 4q + j holds row 8q + 4*(l/32) + j,
     // column l%32; four consecutive rows per q go out as one 16-byte store
@@ -234,7 +270,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_mfma_kernel(const GemmArgs 
     }
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int KS = 1>
 static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                            const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
     GemmArgs a{};
@@ -256,19 +292,22 @@ static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8
     a.xq = xq;
     a.xs = xs;
     a.xsum = xsum;
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, S>), dim3((unsigned)tiles), dim3(WM * WN * 64),
-                       0, st, a);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, S, KS>), dim3((unsigned)tiles),
+                       dim3(WM * WN * KS * 64), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    // Token tile matched to small N so no MFMA column work is wasted.
-    // Token counts of batched decode: small row tiles, so that a launch over
-    // a 2B-class layer's matrices still spreads over the CUs (128-row tiles
-    // gave 108 workgroups for the gate/up pair and measured 20-25% slower).
-    if (N <= 32) return run_gemm<32, 32, 1, 1, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-    if (N <= 64) return run_gemm<64, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    // Batched decode token counts (17..64): small row tiles, so that a launch
+    // over a 2B-class layer's matrices spreads over the CUs, and K split over
+    // 4 (32x32 tiles) or 2 (64x64) wave groups inside the workgroup.  Such
+    // launches hold one workgroup per CU, whose waves otherwise spend each
+    // block waiting on one barrier / LDS read / MFMA chain; more stages or a
+    // second accumulator did not help.  Against 128-row tiles without the
+    // split: 20-35% less time per 2B-class step at N = 32..64.
+    if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    if (N <= 64) return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
     // The K loop is bound by the LDS-DMA fills (removing its MFMAs leaves
     // three quarters of its time), so larger tiles -- more MFMA work per
     // staged byte -- win where there are enough of them: 256x128 tiles of

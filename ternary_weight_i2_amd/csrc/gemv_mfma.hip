@@ -5,7 +5,7 @@
 // columns); [P2] "[분석/검증-3]" §3 and [P3] "[기술 분석 보고서]" §3.2 (raw codes
 // multiply the activations; the exact result subtracts sum(x)).
 //
-// At 3..24 tokens every packed byte feeds 24..192 int8 operations, more than
+// At 3..16 tokens every packed byte feeds 24..128 int8 operations, more than
 // the vector ALUs sustain at HBM speed, so the contraction runs on
 // v_mfma_i32_16x16x64_i8 while the weights still stream from HBM once.
 // Larger batches (to 64) go to the prefill GEMM with small tiles (below).
@@ -32,7 +32,7 @@
 
 namespace bitnet {
 
-constexpr int kDecodeGemmMinN = 24;   // larger batches go to the small-tile GEMM
+constexpr int kDecodeMaxN = 16;   // larger batches go to the small-tile GEMM
 
 template <int MI, int NJ, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a) {
@@ -204,14 +204,13 @@ static hipError_t run_nj(const GemmMat *mats, int nmats, int64_t K, const int8_t
 
 hipError_t launch_gemv_mfma(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    // Above kDecodeGemmMinN tokens this kernel's per-lane token loads (every
+    // Above kDecodeMaxN tokens this kernel's per-lane token loads (every
     // 16-row workgroup re-reads all tokens through L1) cost more than the
-    // prefill GEMM's LDS-staged token tiles: on a 2B-class layer at N = 32 /
-    // 48 / 64 the small-tile GEMM takes 7% / 12% / 32% less time per step,
-    // while at N <= 16 this kernel is 25-45% faster.
-    if (N > kDecodeGemmMinN) return launch_gemm_mfma(mats, nmats, K, xq, xs, xsum, N, st);
-    if (N <= 16) return run_nj<1>(mats, nmats, K, xq, xs, xsum, N, st);
-    return run_nj<2>(mats, nmats, K, xq, xs, xsum, N, st);
+    // small-tile, K-split GEMM's LDS-staged token tiles: on a 2B-class layer
+    // the GEMM takes 16% / 22% / 37% less time per step at N = 24 / 32 / 64,
+    // while at N = 16 this kernel is 5% faster.
+    if (N > kDecodeMaxN) return launch_gemm_mfma(mats, nmats, K, xq, xs, xsum, N, st);
+    return run_nj<1>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
 }  // namespace bitnet
