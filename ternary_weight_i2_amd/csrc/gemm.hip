@@ -308,6 +308,14 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     // split: 20-35% less time per 2B-class step at N = 32..64.
     if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     if (N <= 64) return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
+    // A launch with fewer 128x128 tiles than CUs (prefill of a few hundred
+    // tokens) takes the batched-decode tiles: 64x64 with K split in two, four
+    // times the workgroups and twice the waves per tile (the 0.6B-class layer
+    // at N = 128: 51.9 -> 31.2 us; 128x128 tiles with the split: 50.4 us).
+    int64_t t128 = 0;
+    for (int i = 0; i < nmats; ++i) t128 += (mats[i].M + 127) / 128;
+    if (t128 * ((N + 127) / 128) < 256)
+        return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
     // The K loop is bound by the LDS-DMA fills (removing its MFMAs leaves
     // three quarters of its time), so larger tiles -- more MFMA work per
     // staged byte -- win where there are enough of them: 256x128 tiles of
