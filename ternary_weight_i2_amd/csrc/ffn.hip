@@ -38,6 +38,15 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
     const float4 *u4 = reinterpret_cast<const float4 *>(u + row);
     const int nruns = F / 32;
 
+    // The gain of the thread's first run is loaded with g and u, so pass 2
+    // needs no second memory round trip when every run fits one thread
+    // (F <= 8192); further runs load theirs in pass 2.
+    float4 gm0[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        gm0[i] = gamma && tid < nruns ? reinterpret_cast<const float4 *>(gamma)[tid * 8 + i]
+                                      : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+
     for (int r = tid; r < nruns; r += kFfnThreads) {
         double part = 0.0;
 #pragma unroll
@@ -79,8 +88,9 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
         float4 gm[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            gm[i] = gamma ? reinterpret_cast<const float4 *>(gamma)[r * 8 + i]
-                          : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            gm[i] = r == tid ? gm0[i]
+                  : gamma    ? reinterpret_cast<const float4 *>(gamma)[r * 8 + i]
+                             : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float ga[4] = {gm[i].x, gm[i].y, gm[i].z, gm[i].w};
