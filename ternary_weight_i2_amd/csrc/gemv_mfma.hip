@@ -58,6 +58,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
     const int m0 = ((int)blockIdx.x - a.mat[mat].tile_begin) * BM;
     for (int i = tid; i < BM * LDA; i += NT) acc_lds[i] = 0;
 
+    // The epilogue's per-token inputs (sum(x) and 1/s operands) for the E
+    // outputs this thread writes, loaded before the K loop so their latency is
+    // hidden instead of following the reduction.
+    constexpr int E = (BM * BN + NT - 1) / NT;
+    int sxe[E];
+    float sse[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = tid + e * NT;
+        const int n = i / BM;
+        const int nn = (i < BM * BN && n < N) ? n : 0;
+        sxe[e] = xsum[nn];
+        sse[e] = xs[nn];
+    }
+
     const int nblk = K >> 7;
     const int b0 = (int)((int64_t)nblk * wv / WAVES);
     const int b1 = (int)((int64_t)nblk * (wv + 1) / WAVES);
@@ -137,13 +152,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
             for (int r = 0; r < 4; ++r)
                 atomicAdd(&acc_lds[(mi * 16 + 4 * kq + r) * LDA + nj * 16 + li], acc[mi][nj][r]);
     __syncthreads();
-    for (int i = tid; i < BM * BN; i += NT) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = tid + e * NT;
         const int n = i / BM, ml = i - n * BM;
         const int m = m0 + ml;
-        if (n < N && m < M) {
-            const int d = acc_lds[ml * LDA + n] - xsum[n];
+        if (i < BM * BN && n < N && m < M) {
+            const int d = acc_lds[ml * LDA + n] - sxe[e];
             if (dot) dot[(int64_t)n * M + m] = d;
-            if (y) y[(int64_t)n * M + m] = ((float)d * alpha) / xs[n];
+            if (y) y[(int64_t)n * M + m] = ((float)d * alpha) / sse[e];
         }
     }
 }
