@@ -31,7 +31,7 @@
 // already issued the loads of its first row group, so the two memory
 // latencies overlap.  A workgroup usually owns a single row group; where it
 // owns several, each group is loaded and then consumed (a ping-pong register
-// prefetch, BITNET_GEMV_PIPE=1, measured slower on gfx950).
+// prefetch of the next group measured slower on gfx950).
 //
 // Modes: 0 = int8 xq (+ scale and sum) from global memory; 1/2 = fp32/bf16
 // tokens quantised in the prologue with the same arithmetic as the
@@ -51,12 +51,6 @@ constexpr int kLdsBytes = 61440;   // activation staging budget per workgroup (6
 #endif
 #ifndef BITNET_GEMV_LPR
 #define BITNET_GEMV_LPR 0             // 0: pick lanes per row from K
-#endif
-#ifndef BITNET_GEMV_PIPE
-#define BITNET_GEMV_PIPE 0            // 1: ping-pong register prefetch of the next row group
-#endif
-#ifndef BITNET_GEMV_INTERLEAVE
-#define BITNET_GEMV_INTERLEAVE 0      // 1: workgroups take row groups round-robin
 #endif
 
 template <int MODE>
@@ -233,10 +227,6 @@ struct TokenPrologue {
 // at K=2560: 16 lanes x 3 chunks; down at K=6912: 32 x 4), large ones keep
 // J close to 8 (K=8192: 16 x 8; K=28672: 64 x 7).  All J loads of a row group
 // are in flight together.
-#ifndef BITNET_GEMV_XDIRECT
-#define BITNET_GEMV_XDIRECT 0         // 1: mode 0 reads int8 tokens from global memory
-#endif
-
 // JM: chunks per lane per row group (upper bound of J).  JM = 4 is the
 // short-row variant for single-token launches with J <= 4: its chunk loop has
 // no run-time guard (chunks past J carry zeroed weights), so the compiler can
@@ -265,30 +255,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
     const int C = K >> 6;                       // 16-byte chunks per packed row
     const int J = (C + LPR - 1) / LPR;
     const int wg_local = (int)blockIdx.x - a.mat[mi].wg_begin;
-#if BITNET_GEMV_INTERLEAVE
-    // row group g of this workgroup is global row group wg_local + g * nwg:
-    // at any moment the whole launch reads one compact band of the matrix
-    const int nwg = (mi + 1 < a.nmats ? a.mat[mi + 1].wg_begin : (int)gridDim.x) - a.mat[mi].wg_begin;
-    const int GR = RG * kGemvWaves;                 // rows per row group
-    const int ngroups_all = (M + GR - 1) / GR;
-    const int ngroups = wg_local < ngroups_all ? (ngroups_all - wg_local + nwg - 1) / nwg : 0;
-    const int row1 = M;
-    auto group_row = [&](int g) { return (wg_local + g * nwg) * GR + wv * RG + sub; };
-#else
     const int row0 = wg_local * a.rows_per_wg;
     const int row1 = min(M, row0 + a.rows_per_wg);
     // row groups of this wave: rows row0 + (g*4 + wv)*RG + sub
     const int ngroups = (row1 - row0 + RG * kGemvWaves - 1) / (RG * kGemvWaves);
     auto group_row = [&](int g) { return row0 + (g * kGemvWaves + wv) * RG + sub; };
-#endif
     // Every lane issues exactly JM loads per row group, from a clamped (always
     // valid) address; lanes or rows outside the matrix are zeroed after the
     // load.  A fixed, branch-free load count lets the compiler wait for just
     // the row group in use while the next one is still in flight.
     int4 cur[JM];
-#if BITNET_GEMV_PIPE
-    int4 nxt[JM];
-#endif
     auto load_group = [&](int g, int4 *r) {
         const int row = min(group_row(g), M - 1);
         const v4i *prow = reinterpret_cast<const v4i *>(packed + (int64_t)row * (K >> 2));
@@ -302,14 +278,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
     // ---- activations -> LDS (group-major), per-token scale and sum ----
     // Token loads are issued first, then the first row group's weight loads,
     // so the token work below overlaps the weight latency.
-    constexpr bool kDirect = MODE == 0 && BITNET_GEMV_XDIRECT;
-    if constexpr (kDirect) {
-        load_group(0, cur);
-        if (tid < NT && tid < a.ntok) {
-            s_tok[tid] = a.xs_in[tid];
-            sum_tok[tid] = a.xsum_in[tid];
-        }
-    } else if constexpr (MODE == 0) {
+    if constexpr (MODE == 0) {
         const int n16 = a.ntok * (K >> 4);
         const int4 *src = reinterpret_cast<const int4 *>(a.x);
         if (n16 <= 2 * kGemvThreads) {           // two int4 pieces per thread in registers
@@ -370,21 +339,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     if (t < a.ntok) {
-                        int4 x0, x1, x2, x3;
-                        if constexpr (kDirect) {
-                            const int8_t *xg = reinterpret_cast<const int8_t *>(a.x) + t * K +
-                                               kBlock * (cl >> 1) + 16 * (cl & 1);
-                            x0 = *reinterpret_cast<const int4 *>(xg);
-                            x1 = *reinterpret_cast<const int4 *>(xg + 32);
-                            x2 = *reinterpret_cast<const int4 *>(xg + 64);
-                            x3 = *reinterpret_cast<const int4 *>(xg + 96);
-                        } else {
-                            const int8_t *xt = xl + t * K + 16 * cl;
-                            x0 = *reinterpret_cast<const int4 *>(xt);
-                            x1 = *reinterpret_cast<const int4 *>(xt + gstride);
-                            x2 = *reinterpret_cast<const int4 *>(xt + 2 * gstride);
-                            x3 = *reinterpret_cast<const int4 *>(xt + 3 * gstride);
-                        }
+                        const int8_t *xt = xl + t * K + 16 * cl;
+                        const int4 x0 = *reinterpret_cast<const int4 *>(xt);
+                        const int4 x1 = *reinterpret_cast<const int4 *>(xt + gstride);
+                        const int4 x2 = *reinterpret_cast<const int4 *>(xt + 2 * gstride);
+                        const int4 x3 = *reinterpret_cast<const int4 *>(xt + 3 * gstride);
                         const int xv0[4] = {x0.x, x0.y, x0.z, x0.w};
                         const int xv1[4] = {x1.x, x1.y, x1.z, x1.w};
                         const int xv2[4] = {x2.x, x2.y, x2.z, x2.w};
@@ -414,29 +373,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
             }
         }
     };
-    // Default: load a row group, then consume it.  BITNET_GEMV_PIPE=1 keeps two
-    // register buffers in ping-pong (the next group's loads issued before the
-    // current group is used; past the last group the loads repeat the last
-    // group's cached addresses).
-#if !BITNET_GEMV_PIPE
+    // Load a row group, then consume it (the first group's loads were issued
+    // before the activations were staged).
     for (int g = 0; g < ngroups; ++g) {
         if (g > 0) load_group(g, cur);
         compute(g, cur);
     }
-#else
-    if (ngroups == 1) {
-        compute(0, cur);
-    } else {
-        const int last = ngroups - 1;
-        for (int g = 0; g < ngroups; g += 2) {
-            load_group(min(g + 1, last), nxt);
-            compute(g, cur);
-            if (g + 1 > last) break;
-            load_group(min(g + 2, last), cur);
-            compute(g + 1, nxt);
-        }
-    }
-#endif
 }
 
 // One launch of the kernel for NT tokens per pass, token mode MODE and the
