@@ -79,20 +79,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
     const int64_t rowb = K >> 2;
 
     const uint8_t *prow[MI];
-    bool rok[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         const int m = m0 + mi * 16 + li;
-        rok[mi] = m < M;
-        prow[mi] = packed + (int64_t)(rok[mi] ? m : 0) * rowb + (kq & 1) * 16;
+        prow[mi] = packed + (int64_t)(m < M ? m : 0) * rowb + (kq & 1) * 16;
     }
     const int8_t *xrow[NJ];
-    bool tok[NJ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
         const int n = nj * 16 + li;
-        tok[nj] = n < N;
-        xrow[nj] = xq + (int64_t)(tok[nj] ? n : 0) * K + kq * 16;
+        xrow[nj] = xq + (int64_t)(n < N ? n : 0) * K + kq * 16;
     }
 
     v4i acc[MI][NJ];
@@ -101,19 +97,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = v4i{0, 0, 0, 0};
 
-    const v4i z = v4i{0, 0, 0, 0};
+    // Rows past M and tokens past N load row 0 / token 0 (valid addresses)
+    // and are not zeroed: a row or token only feeds its own output row or
+    // column, which is never stored.  Loading without a select lets the
+    // compiler wait for a block only where its MFMAs use it.
     auto load = [&](int b, v4i *A, v4i (*B)[NJ]) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            A[mi] = rok[mi] ? __builtin_nontemporal_load(
-                                  reinterpret_cast<const v4i *>(prow[mi] + (int64_t)b * 32))
-                            : z;
+            A[mi] = __builtin_nontemporal_load(
+                reinterpret_cast<const v4i *>(prow[mi] + (int64_t)b * 32));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj)
-                B[s2][nj] = tok[nj] ? *reinterpret_cast<const v4i *>(xrow[nj] + (int64_t)b * 128 + s2 * 64)
-                                    : z;
+                B[s2][nj] = *reinterpret_cast<const v4i *>(xrow[nj] + (int64_t)b * 128 + s2 * 64);
     };
     auto compute = [&](const v4i *A, v4i (*B)[NJ]) {
 #pragma unroll
