@@ -8,51 +8,81 @@
 namespace bitnet {
 
 // ---------------------------------------------------------------------------
-// Packing [P1 §1-1, §4-2].  One thread builds one packed dword = bytes
-// g0..g0+3 of a 32-byte block, i.e. block positions g0+e+32*i for e, i in
-// 0..3.  For each group i the four source weights are contiguous in the row,
-// so the thread issues four aligned 32-bit loads and one 32-bit store.
-// A weight outside {-1,0,+1} is counted in *bad and stored as code 3.
+// Packing [P1 §1-1, §4-2].  Packed byte g of a 32-byte block holds block
+// positions g, g+32, g+64, g+96; so bytes g0..g0+n-1 of a block come from n
+// contiguous weights at each of the offsets 0, 32, 64, 96, and a thread that
+// builds them issues four aligned loads and one store of n bytes (n = 16
+// when w is 16-byte aligned, else 4).  A weight outside {-1,0,+1} is counted
+// in *bad and stored as code 3.
 // ---------------------------------------------------------------------------
+// WIDE = 1 (w 16-byte aligned): one thread per 16-byte half of a packed
+// block, four 16-byte loads and one 16-byte store.  WIDE = 0: one thread per
+// packed dword, four 4-byte loads and one 4-byte store.
+template <int WIDE>
 __global__ __launch_bounds__(256) void pack_i2s_kernel(
     const int8_t *__restrict__ w, int64_t M, int64_t K,
     uint8_t *__restrict__ packed, unsigned *__restrict__ bad) {
-    const int64_t dw_per_row = K / 16;
-    const int64_t total = M * dw_per_row;
+    constexpr int DW = WIDE ? 4 : 1;                    // packed dwords per thread
+    const int64_t units_per_row = K / (16 * DW);
+    const int64_t total = M * units_per_row;
     unsigned nbad = 0;
     for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < total;
          d += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t m = d / dw_per_row;
-        const int64_t r = d - m * dw_per_row;
-        const int64_t blk = r >> 3;          // 8 dwords per block
-        const int g0 = (int)(r & 7) * 4;     // first block byte of this dword
+        const int64_t m = d / units_per_row;
+        const int64_t r = d - m * units_per_row;
+        const int64_t blk = r / (8 / DW);              // 8 dwords per block
+        const int g0 = (int)(r % (8 / DW)) * 4 * DW;    // first block byte of this unit
         const int8_t *src = w + m * K + blk * kBlock + g0;
-        uint32_t out = 0;
+        uint32_t out[DW];
+        uint32_t v[4][DW];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t v = *reinterpret_cast<const uint32_t *>(src + 32 * i);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                int code = (int)(int8_t)(v >> (8 * e)) + 1;   // -1,0,+1 -> 0,1,2
-                if ((unsigned)code > 2u) {
-                    ++nbad;
-                    code = 3;
-                }
-                out |= (uint32_t)code << (8 * e + 6 - 2 * i);
+            if constexpr (WIDE) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(src + 32 * i);
+                v[i][0] = q.x;
+                v[i][1] = q.y;
+                v[i][2] = q.z;
+                v[i][3] = q.w;
+            } else {
+                v[i][0] = *reinterpret_cast<const uint32_t *>(src + 32 * i);
             }
         }
-        *reinterpret_cast<uint32_t *>(packed + m * (K / 4) + blk * kBlockBytes + g0) = out;
+#pragma unroll
+        for (int t = 0; t < DW; ++t) {
+            out[t] = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    int code = (int)(int8_t)(v[i][t] >> (8 * e)) + 1;   // -1,0,+1 -> 0,1,2
+                    if ((unsigned)code > 2u) {
+                        ++nbad;
+                        code = 3;
+                    }
+                    out[t] |= (uint32_t)code << (8 * e + 6 - 2 * i);
+                }
+        }
+        uint8_t *dst = packed + m * (K / 4) + blk * kBlockBytes + g0;
+        if constexpr (WIDE)
+            *reinterpret_cast<uint4 *>(dst) = uint4{out[0], out[1], out[2], out[3]};
+        else
+            *reinterpret_cast<uint32_t *>(dst) = out[0];
     }
     if (nbad) atomicAdd(bad, nbad);
 }
 
 hipError_t launch_pack(const int8_t *w, int64_t M, int64_t K, uint8_t *packed,
                        unsigned *bad, hipStream_t st) {
-    const int64_t total = M * (K / 16);
+    const bool wide = (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+    const int64_t total = M * (K / (wide ? 64 : 16));
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(pack_i2s_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                       w, M, K, packed, bad);
+    if (wide)
+        hipLaunchKernelGGL(pack_i2s_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, w, M, K,
+                           packed, bad);
+    else
+        hipLaunchKernelGGL(pack_i2s_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, w, M, K,
+                           packed, bad);
     return hipGetLastError();
 }
 

@@ -100,6 +100,22 @@ def test_pack_bit_exact(bn, M, K):
         np.testing.assert_array_equal(P, Pr)
 
 
+def test_pack_unaligned_source(bn):
+    """w only 4-byte aligned (the narrow one-dword-per-thread path)."""
+    rng = np.random.default_rng(17)
+    M, K = 37, 640
+    W = synth.ternary(rng, M, K)
+    buf = torch.zeros(M * K + 16, dtype=torch.int8, device="cuda")
+    view = buf[4:4 + M * K].view(M, K)
+    view.copy_(dev(W))
+    assert view.data_ptr() % 16 == 4
+    P = bn.pack(view)
+    torch.cuda.synchronize()
+    Pr, bad = oracle.pack_i2s(W)
+    assert bad == 0
+    np.testing.assert_array_equal(P.cpu().numpy(), Pr)
+
+
 def test_pack_rejects_non_ternary(bn):
     W = np.zeros((5, 256), dtype=np.int8)
     W[3, 17] = 2
