@@ -578,8 +578,9 @@ def row_prefill(bn, synth, torch, stack):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the sharded layout is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "splitting the matrices across GPUs (by rows, or by K with an int32 "
+              "all-reduce before the epilogue) is not implemented.", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_probe:
