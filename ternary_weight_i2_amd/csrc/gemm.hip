@@ -31,6 +31,11 @@
 // the factor computed once per token before the main loop (two fp32
 // roundings, as D * alpha / s has; a division per output made the epilogue
 // VALU-bound).
+//
+// K groups (KS > 1): for launches too small to fill the CUs (batched decode,
+// prefill of a few hundred tokens) a workgroup holds KS groups of WM x WN
+// waves that take alternate blocks of K through their own stages; the
+// groups' int32 partial sums meet in LDS and group 0 writes the tile.
 #include "common.h"
 
 namespace bitnet {
