@@ -33,6 +33,8 @@
 namespace bitnet {
 
 constexpr int kDecodeMaxN = 16;   // larger batches go to the small-tile GEMM
+constexpr int kCus = 256;         // MI355X compute units
+constexpr int kWaveSlots = 32;    // waves resident per CU (8 per SIMD)
 
 template <int MI, int NJ, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a) {
@@ -208,14 +210,20 @@ static hipError_t run_nj(const GemmMat *mats, int nmats, int64_t K, const int8_t
     // reduction (2-3% less time per 2B-class step than eight waves).
     const int64_t nblk = K / 128;
     const int waves = nblk >= 32 ? 16 : (nblk > 16 && nblk <= 20) ? 10 : (nblk >= 16 ? 8 : 4);
-    // rows per workgroup: small matrices keep 16 rows per group (most groups in
-    // flight at once); a launch whose matrices are all large takes 32 so each
-    // token tile is reused twice
-    int64_t min_m = INT64_MAX;
+    // rows per workgroup: 16 (most workgroups in flight at once), or 32 --
+    // each token tile reused twice -- when the matrices are all large or when
+    // 16-row workgroups would not all be resident at once (the grouped
+    // gate/up launch of a 2B-class layer: 864 ten-wave workgroups against
+    // 3 per CU; 32 rows: 3-6% less time per step)
+    int64_t min_m = INT64_MAX, tiles16 = 0;
     for (int i = 0; i < nmats; ++i)
-        if (mats[i].M > 0 && mats[i].M < min_m) min_m = mats[i].M;
+        if (mats[i].M > 0) {
+            if (mats[i].M < min_m) min_m = mats[i].M;
+            tiles16 += (mats[i].M + 15) / 16;
+        }
+    const int64_t resident = (int64_t)kCus * (kWaveSlots / waves);
     if constexpr (NJ <= 2)
-        if (min_m >= 8192 && min_m != INT64_MAX)
+        if ((min_m >= 8192 && min_m != INT64_MAX) || tiles16 > resident)
             return run_w<2, NJ>(waves, mats, nmats, K, xq, xs, xsum, N, st);
     return run_w<1, NJ>(waves, mats, nmats, K, xq, xs, xsum, N, st);
 }
