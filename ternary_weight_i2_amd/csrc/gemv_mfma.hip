@@ -33,6 +33,7 @@
 namespace bitnet {
 
 constexpr int kDecodeMaxN = 16;   // larger batches go to the small-tile GEMM
+constexpr int64_t kDecodeGemmMinK = 8192;   // so do long reductions
 constexpr int kCus = 256;         // MI355X compute units
 constexpr int kWaveSlots = 32;    // waves resident per CU (8 per SIMD)
 
@@ -235,7 +236,15 @@ hipError_t launch_gemv_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     // small-tile, K-split GEMM's LDS-staged token tiles: on a 2B-class layer
     // the GEMM takes 16% / 22% / 37% less time per step at N = 24 / 32 / 64,
     // while at N = 16 this kernel is 5% faster.
-    if (N > kDecodeMaxN) return launch_gemm_mfma(mats, nmats, K, xq, xs, xsum, N, st);
+    //
+    // At K >= kDecodeGemmMinK (the large-layer shapes, 8192 and 28672) the
+    // GEMM is faster at every token count: each of this kernel's 32-row
+    // workgroups re-reads all tokens (2 x the weight bytes at N = 16), the
+    // GEMM's tiles stage them once; three large layers, N = 3 / 4 / 8 / 16:
+    // 320 / 328 / 354 / 407 us -> 295 / 296 / 298 / 305 us.  At K = 6912
+    // (the 2B-class down projection, 2560 rows) it is 10-15% slower.
+    if (N > kDecodeMaxN || K >= kDecodeGemmMinK)
+        return launch_gemm_mfma(mats, nmats, K, xq, xs, xsum, N, st);
     return run_nj<1>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
