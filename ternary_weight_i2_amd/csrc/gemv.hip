@@ -89,7 +89,9 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
         if (wg == 0) continue;
         hipError_t e;
         const unsigned g = (unsigned)wg;
-        const bool sr = nt == 1 && (C + lpr - 1) / lpr <= 4;   // J <= 4: short-row kernels
+        // J <= 4: short-row kernels with exactly 3 or 4 chunk slots
+        const int jn = (C + lpr - 1) / lpr;
+        const int sr = nt == 1 && jn <= 4 ? (jn <= 3 ? 3 : 4) : 0;
         if (nt == 1)
             e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, sr, g, st)
               : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, sr, g, st) : launch_gemv_nt<1, 2>(a, lpr, sr, g, st);

@@ -227,14 +227,14 @@ struct TokenPrologue {
 // at K=2560: 16 lanes x 3 chunks; down at K=6912: 32 x 4), large ones keep
 // J close to 8 (K=8192: 16 x 8; K=28672: 64 x 7).  All J loads of a row group
 // are in flight together.
-// JM: chunks per lane per row group (upper bound of J).  JM = 4 is the
-// short-row variant for single-token launches with J <= 4: its chunk loop has
-// no run-time guard (chunks past J carry zeroed weights), so the compiler can
-// issue every chunk's LDS reads at once -- the tail after the weights arrive
-// is a latency chain in these small launches.
+// JM: chunks per lane per row group (upper bound of J).  JM = 3 or 4 are the
+// short-row variants for single-token launches with J <= 3 / J = 4: their
+// chunk loop has no run-time guard (chunks past J carry zeroed weights), so
+// the compiler can issue every chunk's LDS reads at once -- the tail after the
+// weights arrive is a latency chain in these small launches.
 template <int NT, int LPR, int MODE, int JM>
 __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs a) {
-    constexpr bool kAllChunks = JM == 4;
+    constexpr bool kAllChunks = JM <= 4;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
     int8_t *xl = reinterpret_cast<int8_t *>(lds);
@@ -401,15 +401,17 @@ static hipError_t launch_gemv_ntj(const GemvArgs &a, int lpr, unsigned grid, hip
 // Each (NT, MODE) pair is instantiated in one of the gemv_valu_n*.hip
 // translation units.
 template <int NT, int MODE>
-hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, bool short_rows, unsigned grid,
+hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, unsigned grid,
                           hipStream_t st) {
-    if constexpr (NT == 1)
-        if (short_rows) return launch_gemv_ntj<NT, MODE, 4>(a, lpr, grid, st);
+    if constexpr (NT == 1) {
+        if (short_j == 3) return launch_gemv_ntj<NT, MODE, 3>(a, lpr, grid, st);
+        if (short_j == 4) return launch_gemv_ntj<NT, MODE, 4>(a, lpr, grid, st);
+    }
     return launch_gemv_ntj<NT, MODE, 8>(a, lpr, grid, st);
 }
 
 #define BITNET_GEMV_EXTERN(NT, MODE) \
-    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, bool, unsigned, hipStream_t)
+    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, int, unsigned, hipStream_t)
 // passes of one or two tokens (larger batches run on MFMA)
 BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);
 BITNET_GEMV_EXTERN(2, 0); BITNET_GEMV_EXTERN(2, 1); BITNET_GEMV_EXTERN(2, 2);
