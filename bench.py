@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "d9e71a539deec5cd60cbc9b129213cd3088f859ae1ebc7386e511da0ac52d8aa",
-           "bytes_per_launch": 4578816}
+           "sha256": "fe0d550d6a3403853788f45c253233e62748955a3656a4173d0d527602d91fe0",
+           "bytes_per_launch": 4576512}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
