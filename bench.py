@@ -169,6 +169,31 @@ def time_graph(torch, g, reps, warmup):
     return e0.elapsed_time(e1) / 1e3      # seconds
 
 
+def device_context(torch):
+    """The device, and the read rate torch's own sum reaches on 1 GiB of fp32:
+    a library read stream for context, not a ceiling (the large-layer GEMV
+    row reads faster)."""
+    props = torch.cuda.get_device_properties(0)
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(10):
+        x.sum()
+    e1.record(st)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / 10
+    del x
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "torch_sum_read_GBs": round((1 << 30) / t / 1e9, 1),
+            "torch_sum_read_method": "torch sum over 1 GiB fp32, 10 reps"}
+
+
 def cpu_baseline(seconds):
     """The CPU oracle (as written) on a bounded sample: layer 0 of the same
     stack, drawn on the host, quantised and multiplied with all threads."""
@@ -615,6 +640,22 @@ def main():
     per_launch_s = el / (args.steps * launches)
     achieved = sbytes / launches / per_launch_s / 1e9
 
+    # spread: the same graph replayed one step at a time (each figure also
+    # holds the graph's own launch latency)
+    st = torch.cuda.current_stream()
+    single = []
+    for _ in range(max(20, min(args.steps, 100))):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g_step.replay()
+        e1.record(st)
+        e1.synchronize()
+        single.append(e0.elapsed_time(e1))
+    single.sort()
+    pct = {f"p{q}": round(single[int(q / 100 * (len(single) - 1))], 4) for q in (10, 50, 90)}
+    context = device_context(torch)
+
     # context: the same work through the unfused calls, in a graph, and eager
     g_unf = capture(torch, lambda: run_step_unfused(bn, stack))
     unfused_ms = time_graph(torch, g_unf, args.steps, args.warmup) / args.steps * 1e3
@@ -657,6 +698,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(per_launch_s * 1e6, 3)},
         "cpu_baseline": cpu,
+        "single_step_ms": pct,
+        "context": context,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
