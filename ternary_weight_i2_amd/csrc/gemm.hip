@@ -12,12 +12,13 @@
 //
 // Operand layout.  For MFMA step s of a block (32 k each, s = 0..3) lane
 // (r, kg) -- r = lane%32, kg = lane/32 -- supplies 16 bytes for k = 32s + 16kg
-// + 0..15 of row/token r.  The B operand (tokens) is therefore a plain
-// 16-byte copy of the token row; tokens are staged in LDS in their natural
-// order, with an XOR swizzle of the 16-byte pieces inside a row so a wave's
-// reads spread over the banks.  The contraction is order-free, so the A
-// operand is built to match: those 16 positions are the 2-bit field s of the
-// 16 packed bytes of half kg of the row's block.  One 16-byte read of the
+// + 0..15 of row/token r (the A and B operands take the same lane layout).
+// The token operand (A) is therefore a plain 16-byte copy of the token row;
+// tokens are staged in LDS in their natural order, with an XOR swizzle of the
+// 16-byte pieces inside a row so a wave's reads spread over the banks.  The
+// contraction is order-free, so the weight operand (B) is built to match:
+// those 16 positions are the 2-bit field s of the 16 packed bytes of half kg
+// of the row's block.  One 16-byte read of the
 // packed weight tile per lane per block serves all four steps (shift by 6-2s
 // and mask per dword, no shuffle); the weights are never re-laid out.
 //
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int nj = 0; nj < NJ; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mi], bf[s][nj],
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[s][nj], af[mi],
                                                                         acc[mi][nj], 0, 0, 0);
         }
     }
@@ -234,40 +235,37 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
         }
     }
 
-    // 32x32 result layout: lane l, register 4q + j holds row 8q + 4*(l/32) + j,
-    // column l%32; four consecutive rows per q go out as one 16-byte store
-    // where the output rows allow it.
-    const bool vec_ok = (M & 3) == 0 && ((reinterpret_cast<uintptr_t>(dot) |
-                                          reinterpret_cast<uintptr_t>(y)) & 15) == 0;
+    // Result layout (tokens are the MFMA's A operand): lane l, register 4q + j
+    // holds token 8q + 4*(l/32) + j of the fragment and weight row l%32, so
+    // each dword store writes 32 consecutive outputs of two token rows -- two
+    // whole 128-byte segments.  (Weights as the A operand put four rows of one
+    // token in a lane: 16-byte stores, but each instruction touching 32 token
+    // rows 32 bytes at a time; with y and D written that took 188 against
+    // 154 us on the 0.6B-class layer at N = 4096.)  Lane t (t < 32) holds
+    // token t's sum(x) and factor; the others get them by lane shuffle.
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
-        const int n = n0 + (wn * NJ + nj) * 32 + r32;
-        if (n >= N) continue;
-        const int sx = sxv[nj];
-        const float c = cfac[nj];
+        const int nb = n0 + (wn * NJ + nj) * 32;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
+        for (int q = 0; q < 4; ++q) {
+            int sx[4];
+            float c[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int mb = m0 + (wm * MI + mi) * 32 + 8 * q + 4 * kg;
-                int d[4];
-                float yv[4];
+            for (int j = 0; j < 4; ++j) {
+                sx[j] = __shfl(sxv[nj], 8 * q + 4 * kg + j);
+                c[j] = __shfl(cfac[nj], 8 * q + 4 * kg + j);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int m = m0 + (wm * MI + mi) * 32 + r32;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    d[j] = acc[mi][nj][4 * q + j] - sx;
-                    yv[j] = (float)d[j] * c;
-                }
-                const int64_t o = (int64_t)n * M + mb;
-                if (vec_ok && mb + 3 < M) {
-                    if (dot) *reinterpret_cast<int4 *>(dot + o) = make_int4(d[0], d[1], d[2], d[3]);
-                    if (y) *reinterpret_cast<float4 *>(y + o) = make_float4(yv[0], yv[1], yv[2], yv[3]);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (mb + j < M) {
-                            if (dot) dot[o + j] = d[j];
-                            if (y) y[o + j] = yv[j];
-                        }
+                    const int n = nb + 8 * q + 4 * kg + j;
+                    if (m < M && n < N) {
+                        const int d = acc[mi][nj][4 * q + j] - sx[j];
+                        const int64_t o = (int64_t)n * M + m;
+                        if (dot) dot[o] = d;
+                        if (y) y[o] = (float)d * c[j];
                     }
                 }
             }
@@ -321,18 +319,19 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     for (int i = 0; i < nmats; ++i) t128 += (mats[i].M + 127) / 128;
     if (t128 * ((N + 127) / 128) < 256)
         return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
-    // The K loop is bound by the LDS-DMA fills (removing its MFMAs leaves
-    // three quarters of its time), so larger tiles -- more MFMA work per
-    // staged byte -- win where there are enough of them: 256x128 tiles of
-    // eight waves (64x64 each; 24 KB per block for 128 MFMAs against 20 KB for
-    // 64 at 128x128) when a launch has at least two per CU (the grouped
-    // q/k/v and gate/up launches of a layer), 128x128 tiles of four waves
-    // otherwise.  256x256 tiles measured slower.
+    // 256x128 tiles of eight waves (64x64 each; 24 KB staged per block for
+    // 128 MFMAs) when a launch has at least two per CU (the grouped q/k/v and
+    // gate/up launches of a layer at N = 4096); 256x64, 128x128 and 256x256
+    // measured slower there.  Otherwise 128x64 tiles of four waves: twice the
+    // workgroups of 128x128, so a CU holds two and one's epilogue stores and
+    // barrier waits overlap the other's K loop (0.6B-class o and down at
+    // N = 4096: 19.0 -> 17.5 and 25.3 -> 23.0 us; q/k/v and gate/up at
+    // N = 1024: 14.5 -> 12.3 and 17.5 -> 15.2 us).
     int64_t big = 0;
     for (int i = 0; i < nmats; ++i) big += (mats[i].M + 255) / 256;
     big *= (N + 127) / 128;
     if (big >= 512) return run_gemm<256, 128, 4, 2, 3>(mats, nmats, K, xq, xs, xsum, N, st);
-    return run_gemm<128, 128, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    return run_gemm<128, 64, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
 }  // namespace bitnet

@@ -544,11 +544,22 @@ def test_pack_f32_rejects_non_finite(bn):
 def test_gemm_group_large_tiles_ragged(bn):
     """A group large enough for the 256x128 tiles (512 of them), with M and N
     that are not multiples of the tile: every row against the per-matrix GEMM
-    (128x128 tiles), sampled rows against the oracle."""
+    (128x64 tiles), sampled rows against the oracle."""
     Ms, K, N = (2500, 1300), 256, 4000
     assert sum((M + 255) // 256 for M in Ms) * ((N + 127) // 128) >= 512
     run_gemm_group(bn, Ms, K, N, seed=4242,
                    rows=[(0, 16), (1284, 16)], want_dot=True)
+
+
+def test_gemm_mid_tiles_ragged(bn):
+    """A launch that takes the 128x64 tiles (at least 256 tiles of 128x128,
+    fewer than 512 of 256x128), with M and N ragged against the tile and fewer
+    K blocks than pipeline stages; sampled rows (including the last, partial
+    row tile) against the oracle."""
+    M, K, N = 520, 384, 6600
+    assert ((M + 127) // 128) * ((N + 127) // 128) >= 256
+    assert ((M + 255) // 256) * ((N + 127) // 128) < 512
+    run_case(bn, M, K, N, "gemm", seed=520, rows=[(0, 64), (250, 70), (456, 64)])
 
 
 @pytest.mark.parametrize("Ms,K,N", [((5, 0, 130), 128, 1), ((640, 640, 2560), 2560, 2),
