@@ -47,6 +47,13 @@ namespace bitnet {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Swizzle of the 16-byte pieces of a 128-byte token row in LDS: slot c' of
+// row r holds piece c' ^ tok_swz(r).  A wave's fragment read takes the same
+// piece of 32 consecutive rows; with this mix no two rows among 8 (128-byte
+// bank window) or 16 (256-byte window) consecutive ones share a slot, where
+// r & 7 left rows r and r + 8 on the same banks of a 256-byte window.
+__device__ __forceinline__ int tok_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
 template <int BM, int BN, int WM, int WN, int kStages, int KS>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const GemmArgs a) {
     static_assert(kStages >= 2, "at least double buffering");
@@ -107,11 +114,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
     const int nit = (nkb + KS - 1) / KS;   // iterations of every group (the last may idle)
 
     // Global source of this lane's 16 bytes in each of the wave's DMA
-    // instructions (byte offset 1024*j of the stage; A first, then B).  Rows
-    // and tokens past the matrix are clamped to the last valid one (their
-    // results are never stored).  Token rows are XOR-swizzled: LDS slot c' of
-    // row r holds piece c' ^ (r & 7), which spreads a wave's B reads over the
-    // banks.
+    // instructions (byte offset 1024*j of the stage; the weight tile first,
+    // then the token tile).  Rows and tokens past the matrix are clamped to
+    // the last valid one (their results are never stored).  Token rows are
+    // swizzled by tok_swz.
     const bool full = wave < T - CMIN * NW;   // this wave issues CMAX, else CMIN
     const int8_t *src[CMAX];
     int64_t step[CMAX];                       // source advance per block
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
             step[c] = kBlockBytes;
         } else {
             const int row = 8 * (j - TA) + (lane >> 3);
-            const int piece = (lane & 7) ^ (row & 7);
+            const int piece = (lane & 7) ^ tok_swz(row);
             src[c] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
             step[c] = kBlock;
         }
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
             for (int nj = 0; nj < NJ; ++nj) {
                 const int row = (wn * NJ + nj) * 32 + r32;
                 bf[s][nj] = *reinterpret_cast<const v4i *>(
-                    sb + row * kBlock + 16 * ((2 * s + kg) ^ (row & 7)));
+                    sb + row * kBlock + 16 * ((2 * s + kg) ^ tok_swz(row)));
             }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
