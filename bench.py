@@ -588,7 +588,7 @@ def row_prefill(bn, synth, torch, stack):
                         for (P, a), (d, y) in zip(mats, o):
                             bn.gemm(P, a, q[0], q[1], q[2], want_dot=d is not None, out=(d, y))
             g = capture(torch, run)
-            t = time_graph(torch, g, 20, 3) / 20
+            t = time_graph(torch, g, 50, 10) / 50   # short graphs: more replays
             del g
             rows[f"prefill_N{N}_{tag}"] = {
                 "workload": "0.6B-class layer q/k/v/o/gate/up/down",
