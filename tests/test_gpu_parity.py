@@ -427,6 +427,18 @@ def test_gemm_group_e06_prefill(bn, group, N):
     run_gemm_group(bn, Ms, K, N, seed=N + len(group), rows=rows, want_dot=(N == 128))
 
 
+@pytest.mark.parametrize("N", [40, 64])
+def test_gemm_group_b2_ffn_33_64(bn, N):
+    """33..64 tokens: the 2B-class gate/up pair in one launch (216 tiles of
+    64x64, which it keeps) against each matrix alone (108 tiles, so 32x32
+    tiles with K split in four), bit for bit, and sampled rows against the
+    oracle."""
+    Ms = (synth.SHAPES["b2"]["gate"][0], synth.SHAPES["b2"]["up"][0])
+    K = synth.SHAPES["b2"]["gate"][1]
+    assert sum((M + 63) // 64 for M in Ms) >= 128 and (Ms[0] + 63) // 64 < 128
+    run_gemm_group(bn, Ms, K, N, seed=6400 + N, rows=[(0, 40), (3000, 33), (Ms[0] - 19, 19)])
+
+
 def test_linear_e06_prefill_layer(bn):
     """The 0.6B-class layer's four prefill calls through bitnet_linear_i2s
     (quantise + grouped GEMM), N=256, sampled rows against the oracle."""
