@@ -154,10 +154,19 @@ def capture(torch, fn):
     return g
 
 
-def time_graph(torch, g, reps, warmup):
+def time_graph(torch, g, reps, warmup, min_warm_s=0.0):
+    """Seconds for ``reps`` replays of ``g`` after ``warmup`` untimed ones
+    (and, for the secondary rows, untimed replays until ``min_warm_s`` of
+    wall time has passed, so a short graph after host-side set-up is not
+    timed while the clocks ramp)."""
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -338,7 +347,7 @@ def row_ffn(bn, synth, torch, stack):
                 else:
                     bn.gemm(P, a, q[0], q[1], q[2], out=out)
         g = capture(torch, run)
-        t = time_graph(torch, g, 10, 3) / 10
+        t = time_graph(torch, g, 10, 3, 0.02) / 10
         del g
         wbytes = sum(m[p][0].numel() for m, _ in layers for p in ("gate", "up", "down"))
         byts = wbytes + 30 * N * (2 * H + 2 * F * 4 + F * 4 + 2 * F + H * 8)
@@ -384,7 +393,7 @@ def row_decode(bn, synth, torch, stack):
             for P, alpha, q, d, yy, M, K in bufs:
                 bn.gemv(P, alpha, q[0], q[1], q[2], out=(d, yy))
         g = capture(torch, run)
-        t = time_graph(torch, g, 10, 3) / 10
+        t = time_graph(torch, g, 10, 3, 0.02) / 10
         byts = sum(M * K // 4 + N * K + N * M * 8 for P, a, q, d, yy, M, K in bufs)
         ops = sum(2 * M * K * N for P, a, q, d, yy, M, K in bufs)
         rows[f"decode_N{N}"] = {"workload": "2B-class stack, 30 layers x 7 GEMVs",
@@ -408,7 +417,7 @@ def row_decode(bn, synth, torch, stack):
             for ms, q, outs, K in groups:
                 bn.gemv_group(ms, q[0], q[1], q[2], out=outs)
         g = capture(torch, run_g)
-        t = time_graph(torch, g, 10, 3) / 10
+        t = time_graph(torch, g, 10, 3, 0.02) / 10
         rows[f"decode_N{N}_grouped"] = {
             "workload": "2B-class stack, 30 layers x 4 grouped launches (q/k/v, o, gate/up, down)",
             "us_per_step": round(t * 1e6, 1), "GB/s": round(byts / t / 1e9, 1),
@@ -433,7 +442,7 @@ def row_decode(bn, synth, torch, stack):
             for xb, ms, outs, q in lin:
                 bn.linear(xb, ms, out=outs, qout=q if N > 2 else None)
         g = capture(torch, run_l)
-        t = time_graph(torch, g, 10, 3) / 10
+        t = time_graph(torch, g, 10, 3, 0.02) / 10
         lbytes = byts + sum(N * xb.shape[1] for xb, ms, outs, q in lin)   # bf16 tokens: one more byte each
         rows[f"decode_N{N}_linear"] = {
             "workload": "2B-class stack, bf16 tokens, bitnet_linear_i2s per dependency group",
@@ -477,7 +486,7 @@ def row_lut(bn, synth, torch, stack):
                 for P, alpha, q, d, yy, M, K in bufs:
                     fn(P, alpha, q[0], q[1], q[2], out=(d, yy))
             g = capture(torch, run)
-            t = time_graph(torch, g, 10, 3) / 10
+            t = time_graph(torch, g, 10, 3, 0.02) / 10
             del g
             rows[f"lut_{tag}_N1_{how}"] = {"workload": what, "us_per_step": round(t * 1e6, 1),
                                            "us_per_launch": round(t * 1e6 / len(bufs), 2),
@@ -529,7 +538,7 @@ def row_large(bn, synth, torch, stack):
                     for (P, a), o in zip(mats, outs):
                         bn.gemv(P, a, q[0], q[1], q[2], out=o)
         g = capture(torch, run)
-        t = time_graph(torch, g, 5, 2) / 5
+        t = time_graph(torch, g, 5, 2, 0.02) / 5
         del g
         K_tok = sum(x.shape[1] for x, q, mats, outs, qout in bufs)
         M_out = sum(P.shape[0] for x, q, mats, outs, qout in bufs for P, _ in mats)
@@ -588,7 +597,7 @@ def row_prefill(bn, synth, torch, stack):
                         for (P, a), (d, y) in zip(mats, o):
                             bn.gemm(P, a, q[0], q[1], q[2], want_dot=d is not None, out=(d, y))
             g = capture(torch, run)
-            t = time_graph(torch, g, 50, 10) / 50   # short graphs: more replays
+            t = time_graph(torch, g, 50, 10, 0.02) / 50   # short graphs: more replays
             del g
             rows[f"prefill_N{N}_{tag}"] = {
                 "workload": "0.6B-class layer q/k/v/o/gate/up/down",

@@ -315,18 +315,18 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     // block waiting on one barrier / LDS read / MFMA chain; more stages or a
     // second accumulator did not help.  Against 128-row tiles without the
     // split: 20-35% less time per 2B-class step at N = 32..64.
-    // For 33..64 tokens the 64x64 tiles are kept only where a launch has at
-    // least 128 of them (the 2B-class gate/up pair: 216); fewer (q/k/v, o,
-    // down: 40-60) leave most CUs idle and take the 32x32 tiles instead
-    // (2B-class layer at N = 64: o 8.3 -> 7.2, down 14.8 -> 9.7 us; gate/up
-    // on 32x32 tiles 9.5 -> 14.0 us).
+    // Above 32 tokens a launch with fewer than 128 tiles of 64x64 (at most
+    // half the CUs busy) still takes the 32x32 tiles, four times the
+    // workgroups (2B-class layer at N = 64: o 8.3 -> 7.2, down 14.8 -> 9.7 us;
+    // 0.6B-class o and down at N = 128: 8.3 -> 7.5 and 9.3 -> 7.4 us); with a
+    // threshold of 256 the gate/up launches (192-216 tiles) went 9.5 -> 14.0
+    // and 8.2 -> 9.4 us.
     if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-    if (N <= 64) {
-        int64_t t64 = 0;
-        for (int i = 0; i < nmats; ++i) t64 += (mats[i].M + 63) / 64;
-        if (t64 < 128) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-        return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
-    }
+    int64_t t64 = 0;
+    for (int i = 0; i < nmats; ++i) t64 += (mats[i].M + 63) / 64;
+    if (t64 * ((N + 63) / 64) < 128)
+        return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    if (N <= 64) return run_gemm<64, 64, 2, 2, 3, 2>(mats, nmats, K, xq, xs, xsum, N, st);
     // A launch with fewer 128x128 tiles than CUs (prefill of a few hundred
     // tokens) takes the batched-decode tiles: 64x64 with K split in two, four
     // times the workgroups and twice the waves per tile (the 0.6B-class layer
