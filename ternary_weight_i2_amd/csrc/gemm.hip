@@ -60,7 +60,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
     static_assert(KS >= 1, "K groups");
     constexpr int NW = WM * WN;        // waves per K group (one output tile)
     constexpr int MI = BM / WM / 32;   // 32-row MFMA tiles per wave
-    constexpr int NJ = BN / WN / 32;   // 32-token MFMA tiles per wave
+    // 32-token MFMA tiles per wave.  A 16-token tile (BN = 16, one wave
+    // column) stages only 16 token rows per block; the MFMA's rows 16..31
+    // re-read rows 0..15 and their results are not stored.
+    constexpr int NJ = BN < 32 ? 1 : BN / WN / 32;
+    static_assert(BN >= 32 || (BN == 16 && WN == 1), "16-token tiles: one wave column");
     static_assert(MI >= 1 && NJ >= 1, "tile too small");
     // LDS-DMA instructions per block (each moves 64 lanes x 16 bytes = 1 KB):
     // TA for the weight tile (BM rows x 32 bytes), TB for the token tile (BN
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj) {
-                const int row = (wn * NJ + nj) * 32 + r32;
+                const int row = BN < 32 ? (r32 & (BN - 1)) : (wn * NJ + nj) * 32 + r32;
                 bf[s][nj] = *reinterpret_cast<const v4i *>(
                     sb + row * kBlock + 16 * ((2 * s + kg) ^ tok_swz(row)));
             }
@@ -254,6 +258,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
         const int nb = n0 + (wn * NJ + nj) * 32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            if (BN < 32 && q >= BN / 8) continue;   // tokens past a 16-token tile
             int sx[4];
             float c[4];
 #pragma unroll
@@ -321,6 +326,18 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     // 0.6B-class o and down at N = 128: 8.3 -> 7.5 and 9.3 -> 7.4 us); with a
     // threshold of 256 the gate/up launches (192-216 tiles) went 9.5 -> 14.0
     // and 8.2 -> 9.4 us.
+    // Up to 16 tokens (the large layer's batched decode at K >= 8192): 16-token
+    // tiles, so each block stages 2 KB of tokens instead of 4 KB for a 32-token
+    // tile of which half is padding; 64 rows per tile where that still gives
+    // every CU a workgroup, else 32 (large layer at N = 16: 987 us per step on
+    // 32x32 tiles, 907 on 32x16, 892 on 64x16).
+    if (N <= 16) {
+        int64_t t64r = 0;
+        for (int i = 0; i < nmats; ++i) t64r += (mats[i].M + 63) / 64;
+        if (t64r * ((N + 15) / 16) >= 256)
+            return run_gemm<64, 16, 2, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+        return run_gemm<32, 16, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    }
     if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     int64_t t64 = 0;
     for (int i = 0; i < nmats; ++i) t64 += (mats[i].M + 63) / 64;

@@ -576,7 +576,9 @@ def test_gemm_mid_tiles_ragged(bn):
 
 @pytest.mark.parametrize("Ms,K,N", [((5, 0, 130), 128, 1), ((640, 640, 2560), 2560, 2),
                                     ((257, 33), 384, 7), ((300, 41, 7), 1280, 24),
-                                    ((64, 0, 90), 512, 25), ((100, 200), 640, 64)])
+                                    ((64, 0, 90), 512, 25), ((100, 200), 640, 64),
+                                    ((100, 33, 65), 8320, 3), ((70,), 8192, 16),
+                                    ((129, 64), 8448, 9)])
 def test_gemv_group(bn, Ms, K, N):
     """Grouped decode GEMV vs bitnet_gemv_i2s_i8 per matrix (bit for bit) and
     the oracle."""
