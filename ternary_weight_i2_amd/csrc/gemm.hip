@@ -336,6 +336,9 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
         for (int i = 0; i < nmats; ++i) t64r += (mats[i].M + 63) / 64;
         if (t64r * ((N + 15) / 16) >= 256)
             return run_gemm<64, 16, 2, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+        // long reductions (the large layer's down projection, K = 28672): K
+        // split over eight wave groups instead of four (877 -> 854 us per step)
+        if (K >= 16384) return run_gemm<32, 16, 1, 1, 3, 8>(mats, nmats, K, xq, xs, xsum, N, st);
         return run_gemm<32, 16, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     }
     if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
