@@ -563,6 +563,16 @@ def test_gemm_group_large_tiles_ragged(bn):
                    rows=[(0, 16), (1284, 16)], want_dot=True)
 
 
+@pytest.mark.parametrize("entry", ["gemm", "gemv"])
+def test_sixteen_token_tiles_ragged(bn, entry):
+    """Up to 16 tokens on the 64x16 GEMM tiles (at least 256 of them; the
+    decode entry takes them at K >= 8192): M ragged against the tile, N = 7;
+    sampled rows including the last, partial row tile, against the oracle."""
+    M, K, N = 16400, 8192, 7
+    assert (M + 63) // 64 >= 256 and M % 64 != 0
+    run_case(bn, M, K, N, entry, seed=1640, rows=[(0, 40), (8190, 20), (M - 30, 30)])
+
+
 def test_gemm_mid_tiles_ragged(bn):
     """A launch that takes the 128x64 tiles (at least 256 tiles of 128x128,
     fewer than 512 of 256x128), with M and N ragged against the tile and fewer
