@@ -225,20 +225,24 @@ def test_special_weights(bn):
         assert (d[:, 80:] == qs[:, None]).all()
 
 
-def test_extreme_activations_max_k(bn):
-    # every activation at +-127 with K = 32768: the largest |D| the ABI allows
-    K, M, N = 32768, 8, 2
+@pytest.mark.parametrize("N", [2, 5, 40])
+def test_extreme_activations_max_k(bn, N):
+    # every activation at +-127 with K = 32768: the largest |D| the ABI allows,
+    # through the fused/VALU decode (N = 2), the 16-token GEMM tiles with K in
+    # eight groups (N = 2 and 5) and the 32x32 tiles (N = 40)
+    K, M = 32768, 8
     W = np.ones((M, K), dtype=np.int8)
     W[1::2] = -1
     x = np.full((N, K), 3.0, dtype=np.float32)
-    x[1] = -3.0
+    x[1::2] = -3.0
     P = bn.pack(dev(W))
     xq, xs, xsum = bn.quant_act(dev(x))
+    sign_n = np.where(np.arange(N) % 2 == 0, 1, -1)
+    sign_m = np.where(np.arange(M) % 2 == 0, 1, -1)
+    expect = 127 * K * sign_n[:, None] * sign_m[None, :]
     for fn in (bn.gemv, bn.gemm):
         dot, _ = fn(P, 1.0, xq, xs, xsum)
-        d = dot.cpu().numpy()
-        assert d[0, 0] == 127 * K and d[0, 1] == -127 * K
-        assert d[1, 0] == -127 * K and d[1, 1] == 127 * K
+        np.testing.assert_array_equal(dot.cpu().numpy(), expect)
 
 
 def test_deterministic(bn):
