@@ -6,9 +6,10 @@
 //
 // Tiling: a workgroup of WM x WN waves computes a BM x BN tile of the output
 // (weight rows x tokens); wave (wm, wn) owns a (32*MI) x (32*NJ) sub-tile made
-// of 32x32 MFMA tiles.  K advances one 128-weight I2_S block at a time.  One
-// launch may serve several matrices that share the tokens (tiles numbered
-// matrix by matrix).
+// of 32x32 MFMA tiles (a 16-token tile, BN = 16, stages only 16 token rows
+// and its MFMAs' other 16 rows re-read them; those results are not stored).
+// K advances one 128-weight I2_S block at a time.  One launch may serve
+// several matrices that share the tokens (tiles numbered matrix by matrix).
 //
 // Operand layout.  For MFMA step s of a block (32 k each, s = 0..3) lane
 // (r, kg) -- r = lane%32, kg = lane/32 -- supplies 16 bytes for k = 32s + 16kg
