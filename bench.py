@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "fe0d550d6a3403853788f45c253233e62748955a3656a4173d0d527602d91fe0",
-           "bytes_per_launch": 4576512}
+           "sha256": "94443fff734bf04c7def389410c6de3d35b95b84addbaf18bf8e63850ec69166",
+           "bytes_per_launch": 4578048}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))

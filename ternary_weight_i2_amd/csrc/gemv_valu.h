@@ -158,7 +158,10 @@ struct TokenPrologue {
         int sm[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            s[t] = quant_scale(fmaxf(fmaxf(redf[0][t], redf[1][t]), fmaxf(redf[2][t], redf[3][t])));
+            float amx = redf[0][t];
+#pragma unroll
+            for (int w = 1; w < kGemvWaves; ++w) amx = fmaxf(amx, redf[w][t]);
+            s[t] = quant_scale(amx);
             sm[t] = 0;
         }
         const bool store = blockIdx.x == 0 && a.xq_out != nullptr;
@@ -209,7 +212,9 @@ struct TokenPrologue {
         }
         __syncthreads();
         if (tid < NT && tid < a.ntok) {
-            const int total = redi[0][tid] + redi[1][tid] + redi[2][tid] + redi[3][tid];
+            int total = 0;
+#pragma unroll
+            for (int w = 0; w < kGemvWaves; ++w) total += redi[w][tid];
             s_tok[tid] = s[tid];
             sum_tok[tid] = total;
             if (blockIdx.x == 0) {
