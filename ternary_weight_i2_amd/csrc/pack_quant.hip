@@ -120,21 +120,24 @@ struct Vec16<1> {
     }
 };
 
+constexpr int kQuantThreads = 256;   // one workgroup per token
+constexpr int kQuantWaves = kQuantThreads / 64;
+
 template <int BF16>
-__global__ __launch_bounds__(256) void quant_act_kernel(
+__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const void *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
     float *__restrict__ xs, int32_t *__restrict__ xsum) {
     using V = Vec16<BF16>;
     constexpr int E = V::kElems;
-    __shared__ float red_f[4];
-    __shared__ int red_i[4];
+    __shared__ float red_f[kQuantWaves];
+    __shared__ int red_i[kQuantWaves];
     const int64_t n = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const char *row = reinterpret_cast<const char *>(x) + n * K * (BF16 ? 2 : 4);
     const int64_t nvec = K / E;
 
     float a = 0.0f;
-    for (int64_t i = tid; i < nvec; i += 256) {
+    for (int64_t i = tid; i < nvec; i += kQuantThreads) {
         float v[E];
         V::load(row, i, v);
 #pragma unroll
@@ -143,12 +146,14 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     a = wave_max_f32(a);
     if (lane == 0) red_f[wv] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    a = red_f[0];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) a = fmaxf(a, red_f[w]);
     const float s = quant_scale(a);
 
     int8_t *qrow = xq + n * K;
     int sum = 0;
-    for (int64_t i = tid; i < nvec; i += 256) {
+    for (int64_t i = tid; i < nvec; i += kQuantThreads) {
         float v[E];
         V::load(row, i, v);
         uint32_t packedq[E / 4];
@@ -171,17 +176,20 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     __syncthreads();
     if (tid == 0) {
         xs[n] = s;
-        xsum[n] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kQuantWaves; ++w) t += red_i[w];
+        xsum[n] = t;
     }
 }
 
 hipError_t launch_quant(const void *x, int bf16, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t st) {
     if (bf16)
-        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)N), dim3(256), 0, st,
+        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)N), dim3(kQuantThreads), 0, st,
                            x, K, xq, xs, xsum);
     else
-        hipLaunchKernelGGL(quant_act_kernel<0>, dim3((unsigned)N), dim3(256), 0, st,
+        hipLaunchKernelGGL(quant_act_kernel<0>, dim3((unsigned)N), dim3(kQuantThreads), 0, st,
                            x, K, xq, xs, xsum);
     return hipGetLastError();
 }
