@@ -347,7 +347,8 @@ LINEAR_CASES = [((7,), 128, 1, "f32"), ((64, 0, 17), 256, 2, "bf16"),
                 ((70, 70), 896, 9, "bf16"), ((65,), 384, 64, "bf16"),
                 ((130, 0, 33), 384, 65, "bf16"), ((200, 129), 640, 300, "f32"),
                 ((3, 5, 7, 9, 11, 13, 15, 17), 512, 3, "bf16"), ((40,), 32768, 2, "f32"),
-                ((300,), 8192, 8, "bf16"), ((129,), 28672, 3, "bf16")]
+                ((300,), 8192, 8, "bf16"), ((129,), 28672, 3, "bf16"),
+                ((257,), 6912, 16, "f32"), ((33, 90), 8064, 16, "bf16")]
 
 
 @pytest.mark.parametrize("Ms,K,N,dtype", LINEAR_CASES)
