@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.orc_unpack_i2s.restype = _i64
         L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_exact_sum.argtypes = [_p, _i64]
+        L.orc_exact_sum.restype = ctypes.c_double
         L.orc_absmean_alpha_f32.argtypes = [_p, _i64]
         L.orc_absmean_alpha_f32.restype = ctypes.c_float
         L.orc_absmean_alpha_bf16.argtypes = [_p, _i64]
@@ -244,6 +246,20 @@ def linear_i2s(packed: np.ndarray, K: int, q: np.ndarray, s: np.ndarray,
     return D, y
 
 
+def exact_sum(x: np.ndarray) -> float:
+    """Exactly rounded binary64 sum of finite, non-negative values (order-free).
+
+    The AbsMean scale [P1 §6-2; P4] and the FFN sub-norm [P4 "Forward Pass"]
+    both sum non-negative values whose order the pages do not fix; the oracle
+    takes the exact sum, rounded once.  Raises on a negative or non-finite value.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float64).ravel()
+    r = lib().orc_exact_sum(_ptr(x), x.size)
+    if r < 0:
+        raise ValueError("exact_sum takes finite, non-negative values")
+    return float(r)
+
+
 def absmean_alpha(w: np.ndarray) -> float:
     """AbsMean scale of a whole tensor [P1 §6-2; P4 "Ternary Weight
     Quantisation (AbsMean)"]: fp32 (float32 array) or bf16 bits (uint16)."""
@@ -288,9 +304,9 @@ def sign_ternary(w: np.ndarray) -> tuple[np.ndarray, float, int]:
 
 
 def ffn_act_quant(g: np.ndarray, u: np.ndarray, gamma, eps: float):
-    """sqrelu(g) * u -> RMS sub-norm (binary64 sum of squares in 32-channel
-    runs, gain gamma or 1) -> per-token int8 quantisation [P4 "Forward Pass";
-    P1 §4-5].  g, u: fp32 [N][F].  Returns (q, s, qsum, v)."""
+    """sqrelu(g) * u -> RMS sub-norm (the exactly rounded binary64 sum of the
+    squares, gain gamma or 1) -> per-token int8 quantisation [P4 "Forward
+    Pass"; P1 §4-5].  g, u: fp32 [N][F].  Returns (q, s, qsum, v)."""
     g = np.ascontiguousarray(g, dtype=np.float32)
     u = np.ascontiguousarray(u, dtype=np.float32)
     N, F = g.shape

@@ -306,6 +306,88 @@ int64_t orc_linear_i2s(const uint8_t *packed, int64_t M, int64_t K,
     return bad;
 }
 
+/* ---- exactly rounded sum of non-negative binary64 values ---- */
+
+/* A fixed-point integer wide enough to hold any sum of finite binary64
+ * values exactly: bit i stands for 2^(i - 1074), the weight of the smallest
+ * subnormal.  1074 + 1024 bits cover every finite value, and 206 more leave
+ * room for far more than 2^63 addends of the largest one. */
+#define ORC_ACC_DIGITS 72
+typedef struct {
+    uint32_t d[ORC_ACC_DIGITS];
+} orc_acc;
+
+/* a += v * 2^(bitpos - 1074), with the carry propagated at once */
+static void acc_add_u32_at(orc_acc *a, int64_t bitpos, uint32_t v)
+{
+    int64_t j = bitpos / 32;
+    uint64_t t = (uint64_t)v << (bitpos % 32);   /* below 2^63 */
+    uint64_t carry = 0;
+    for (; j < ORC_ACC_DIGITS && (t != 0 || carry != 0); j++) {
+        uint64_t s = (uint64_t)a->d[j] + (t & 0xffffffffu) + carry;
+        a->d[j] = (uint32_t)s;
+        carry = s >> 32;
+        t >>= 32;
+    }
+}
+
+/* a += x for a finite x >= 0, exactly */
+static void acc_add(orc_acc *a, double x)
+{
+    if (x == 0.0) return;
+    int e;
+    double f = frexp(x, &e);                      /* x = f * 2^e, 0.5 <= f < 1 */
+    uint64_t m = (uint64_t)ldexp(f, 53);          /* x = m * 2^(e - 53), exactly */
+    int64_t pos = (int64_t)e - 53 + 1074;
+    while (pos < 0) {                             /* a subnormal: m ends in zeros */
+        m >>= 1;
+        pos++;
+    }
+    acc_add_u32_at(a, pos, (uint32_t)(m & 0xffffffffu));
+    acc_add_u32_at(a, pos + 32, (uint32_t)(m >> 32));
+}
+
+static int acc_bit(const orc_acc *a, int64_t i)
+{
+    return (int)((a->d[i / 32] >> (i % 32)) & 1u);
+}
+
+/* the accumulated value rounded once to binary64, to nearest, ties to even */
+static double acc_round(const orc_acc *a)
+{
+    int64_t top = -1;
+    for (int64_t i = (int64_t)ORC_ACC_DIGITS * 32 - 1; i >= 0; i--) {
+        if (acc_bit(a, i)) {
+            top = i;
+            break;
+        }
+    }
+    if (top < 0) return 0.0;
+    if (top < 53) {                               /* below 2^53 units: exact */
+        uint64_t v = 0;
+        for (int64_t i = top; i >= 0; i--) v = 2 * v + (uint64_t)acc_bit(a, i);
+        return ldexp((double)v, -1074);
+    }
+    uint64_t keep = 0;                            /* the 53 leading bits */
+    for (int64_t i = top; i > top - 53; i--) keep = 2 * keep + (uint64_t)acc_bit(a, i);
+    int round = acc_bit(a, top - 53);
+    int sticky = 0;
+    for (int64_t i = top - 54; i >= 0 && !sticky; i--) sticky = acc_bit(a, i);
+    if (round && (sticky || (keep & 1u))) keep++;
+    return ldexp((double)keep, (int)(top - 52 - 1074));
+}
+
+double orc_exact_sum(const double *x, int64_t n)
+{
+    orc_acc acc;
+    memset(&acc, 0, sizeof acc);
+    for (int64_t i = 0; i < n; i++) {
+        if (!(x[i] >= 0.0) || isinf(x[i])) return -1.0;
+        acc_add(&acc, x[i]);
+    }
+    return acc_round(&acc);
+}
+
 /* ---- AbsMean ternariser and sign/threshold ternary (weight conversion) ---- */
 
 static float absmean_from_sum(double sum, int64_t n)
@@ -315,18 +397,28 @@ static float absmean_from_sum(double sum, int64_t n)
     return a > 1e-5f ? a : 1e-5f;
 }
 
+/* Non-finite weights make the result NaN (the caller reports an error). */
 float orc_absmean_alpha_f32(const float *w, int64_t n)
 {
-    double sum = 0.0;
-    for (int64_t i = 0; i < n; i++) sum += fabs((double)w[i]);
-    return absmean_from_sum(sum, n);
+    orc_acc acc;
+    memset(&acc, 0, sizeof acc);
+    for (int64_t i = 0; i < n; i++) {
+        if (!isfinite(w[i])) return NAN;
+        acc_add(&acc, fabs((double)w[i]));
+    }
+    return absmean_from_sum(acc_round(&acc), n);
 }
 
 float orc_absmean_alpha_bf16(const uint16_t *w, int64_t n)
 {
-    double sum = 0.0;
-    for (int64_t i = 0; i < n; i++) sum += fabs((double)orc_bf16_to_f32(w[i]));
-    return absmean_from_sum(sum, n);
+    orc_acc acc;
+    memset(&acc, 0, sizeof acc);
+    for (int64_t i = 0; i < n; i++) {
+        float v = orc_bf16_to_f32(w[i]);
+        if (!isfinite(v)) return NAN;
+        acc_add(&acc, fabs((double)v));
+    }
+    return absmean_from_sum(acc_round(&acc), n);
 }
 
 static int8_t ternary_of(float v, float alpha)
@@ -387,14 +479,13 @@ void orc_ffn_act_quant(const float *g, const float *u, const float *gamma, float
             float r2 = r * r;
             h[k] = r2 * un[k];
         }
-        /* ffn_sub_norm: RMS normalisation over the F channels; binary64
-         * accumulation of the (exact) squares in the stated order */
-        double ss = 0.0;
-        for (int64_t c0 = 0; c0 < F; c0 += 32) {
-            double part = 0.0;
-            for (int64_t k = c0; k < c0 + 32; k++) part += (double)h[k] * (double)h[k];
-            ss += part;
-        }
+        /* ffn_sub_norm: RMS normalisation over the F channels.  Every h^2 is
+         * exact in binary64 (24-bit significands); their sum is taken exactly
+         * and rounded once, so it does not depend on any summation order. */
+        orc_acc acc;
+        memset(&acc, 0, sizeof acc);
+        for (int64_t k = 0; k < F; k++) acc_add(&acc, (double)h[k] * (double)h[k]);
+        double ss = acc_round(&acc);
         float c = (float)(1.0 / sqrt(ss / (double)F + (double)eps));
         for (int64_t k = 0; k < F; k++) {
             float t = h[k] * c;

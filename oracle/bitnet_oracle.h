@@ -103,14 +103,21 @@ int64_t orc_linear_i2s(const uint8_t *packed, int64_t M, int64_t K,
                        int64_t row0, int64_t nrows,
                        int64_t *D, double *y, int nthreads);
 
+/* The sum of n finite, non-negative binary64 values, computed exactly and
+ * rounded once to binary64 (to nearest, ties to even): the result does not
+ * depend on the order of the values.  Returns -1 if a value is negative or
+ * not finite.  Used by the AbsMean scale and the FFN sub-norm below. */
+double orc_exact_sum(const double *x, int64_t n);
+
 /* AbsMean ternarisation of full-precision weights [P1 §6-2; P4 "Ternary
  * Weight Quantisation (AbsMean)"], over all n weights of a tensor:
- *   alpha = max(mean |w|, 1e-5): the sum of |w| in binary64, divided by n in
- *           binary64, rounded once to fp32, then the 1e-5 floor (fp32);
+ *   alpha = max(mean |w|, 1e-5): the exactly rounded binary64 sum of |w|
+ *           (orc_exact_sum), divided by n in binary64, rounded once to fp32,
+ *           then the 1e-5 floor (fp32);
  *   q     = clip(round-half-even(w / alpha), -1, 1), w / alpha one fp32
  *           division.
  * Returns alpha; orc_absmean_ternary writes q.  Non-finite weights make alpha
- * non-finite (the caller treats that as an error). */
+ * NaN (the caller treats that as an error). */
 float orc_absmean_alpha_f32(const float *w, int64_t n);
 float orc_absmean_alpha_bf16(const uint16_t *w, int64_t n);
 void orc_absmean_ternary_f32(const float *w, int64_t n, float alpha, int8_t *q);
@@ -126,8 +133,8 @@ int64_t orc_sign_ternary_f32(const float *w, int64_t n, int8_t *q, float *wmax);
  * "Forward Pass": inner = ffn_sub_norm(sqrelu(gate(x)) (x) up(x)),
  * out = down(inner)], per token n over F channels (F a multiple of 32):
  *   r_k = max(g_k, 0);  h_k = (r_k * r_k) * u_k                    (fp32)
- *   ss  = sum of h_k^2 in binary64 -- each run of 32 consecutive channels
- *         summed in index order, then the run sums in index order
+ *   ss  = sum of h_k^2 (each exact in binary64), computed exactly and
+ *         rounded once to binary64 (orc_exact_sum): no summation order
  *   c   = fp32(1 / sqrt(ss / F + eps))   (binary64, one final rounding)
  *   v_k = (h_k * c) * gamma_k            (fp32; gamma NULL means 1)
  * then v is quantised per token exactly as orc_quant_act_f32 does.

@@ -362,6 +362,32 @@ def test_quant_round_half_even(orc):
     assert q[0, :4].tolist() == [127, 64, -64, 32]
 
 
+def test_quant_multiply_form_not_divide(orc):
+    """"BitNet 딥다이브" §4-5 quantises with the multiplier s = 127/absmax
+    (q = round(x*s)); "bitnet.rs" divides by alpha = absmax/127.  On the stored
+    elements the two fp32 forms round to codes one apart; the oracle must give
+    the multiply form's code (reading: the multiplier of §4-5)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "quant_mul_vs_div.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                a, x = (int(t, 16) for t in line.split())
+                rows.append((np.uint32(a).view(np.float32), np.uint32(x).view(np.float32)))
+    assert len(rows) >= 2
+    for amax, xv in rows:
+        tok = np.zeros((1, 128), np.float32)
+        tok[0, 0] = amax
+        tok[0, 1] = xv
+        s_mul = np.float32(127.0 / np.float64(amax))          # correctly rounded quotient
+        alpha = np.float32(np.float64(amax) / 127.0)
+        q_mul = int(np.rint(np.float32(xv) * s_mul))
+        q_div = int(np.rint(np.float32(xv) / alpha))
+        assert abs(q_mul - q_div) == 1                        # the forms disagree here
+        q, s, _ = orc.quant_act(tok)
+        assert s[0] == s_mul
+        assert int(q[0, 1]) == q_mul
+
+
 def test_quant_rounding_error_bound(orc):
     # |x - q/s| <= 0.5/s elementwise (rounding to nearest), q within [-127,127].
     rng = np.random.default_rng(17)
@@ -561,6 +587,46 @@ def test_absmean_bf16_is_f32_of_widened_bits(orc):
                                   orc.absmean_ternary(wide, orc.absmean_alpha(wide)))
 
 
+def test_absmean_equals_fsum_definition(orc):
+    """alpha = fp32(S / n) with S the exactly rounded binary64 sum of |w|:
+    checked against math.fsum (an independent exactly rounded sum) on random
+    tensors, fp32 and bf16."""
+    import math
+    rng = np.random.default_rng(61)
+    for shape in ((3, 128), (17, 640), (64, 1024)):
+        W = (rng.standard_normal(shape) * 0.05).astype(np.float32)
+        S = math.fsum(np.abs(W.astype(np.float64)).ravel())
+        assert orc.absmean_alpha(W) == max(np.float32(S / W.size), np.float32(1e-5))
+        bits = synth.f32_to_bf16_bits(W)
+        Sb = math.fsum(np.abs(synth.bf16_bits_to_f32(bits).astype(np.float64)).ravel())
+        assert orc.absmean_alpha(bits) == max(np.float32(Sb / W.size), np.float32(1e-5))
+
+
+def test_absmean_sum_is_order_free(orc):
+    """w = [4, 2^-22, 2^-51, 2^-51]: the exact sum is 4 + 2^-22 + 2^-50 (one
+    binary64 ulp above 4 + 2^-22), so the mean 1 + 2^-24 + 2^-52 lies above
+    the fp32 midpoint 1 + 2^-24 and alpha = 1 + 2^-23.  Summed left to right in
+    binary64 each 2^-51 is a tie that rounds away (mean exactly the midpoint,
+    alpha = 1); summed right to left they survive.  The oracle gives
+    1 + 2^-23 for every order."""
+    import itertools
+    base = np.array([4.0, 2.0 ** -22, 2.0 ** -51, 2.0 ** -51], np.float32)
+    want = np.float32(1 + 2.0 ** -23)
+    naive = set()
+    for perm in itertools.permutations(range(4)):
+        w = base[list(perm)]
+        assert orc.absmean_alpha(w) == want
+        acc = 0.0
+        for v in w.astype(np.float64):
+            acc += v
+        naive.add(float(np.float32(acc / 4)))
+    assert naive == {1.0, float(want)}      # a fixed-order binary64 sum depends on the order
+    # the same weights in a 1 x 128 tensor (the rest zero): alpha = (1 + 2^-23) / 32
+    w128 = np.zeros((1, 128), np.float32)
+    w128[0, :4] = base
+    assert orc.absmean_alpha(w128) == want / np.float32(32)
+
+
 # ------------------------------------------- sign/threshold float packer
 def test_sign_ternary_threshold_edges(orc):
     """[P1 §4-2]: |v| < 1e-6 is zero, positive -> +1, negative -> -1; the
@@ -585,6 +651,63 @@ def test_sign_ternary_of_scaled_ternary_round_trips(orc):
     q, wmax, bad = orc.sign_ternary(W)
     np.testing.assert_array_equal(q, T)
     assert bad == 0 and wmax == np.float32(0.0731)
+
+
+# ------------------------------------------- exactly rounded sums
+def test_exact_sum_matches_fsum(orc):
+    """orc_exact_sum against math.fsum (Shewchuk's exactly rounded sum in the
+    Python library) on non-negative values spanning the whole binary64 range,
+    subnormals included."""
+    import math
+    rng = np.random.default_rng(71)
+    for trial in range(300):
+        n = int(rng.integers(1, 400))
+        e = rng.integers(-1074, 1000, size=n) if trial % 3 == 0 else rng.integers(-80, 40, size=n)
+        x = np.ldexp(rng.random(n) + 0.5, e)
+        x[rng.random(n) < 0.1] = 0.0
+        assert orc.exact_sum(x) == math.fsum(x)
+    # squares of fp32 values, as the FFN sub-norm forms them
+    h = (rng.standard_normal(6912) * np.exp2(rng.integers(-30, 10, 6912))).astype(np.float32)
+    sq = h.astype(np.float64) ** 2
+    assert orc.exact_sum(sq) == math.fsum(sq)
+
+
+def test_exact_sum_rounds_half_to_even(orc):
+    one = 1.0
+    ulp = 2.0 ** -52
+    tiny = 5e-324
+    # 1 + 2^-53 is a midpoint: ties to even keep 1; anything above goes up
+    assert orc.exact_sum(np.array([one, 2.0 ** -53])) == one
+    assert orc.exact_sum(np.array([one, 2.0 ** -53, tiny])) == one + ulp
+    # (1 + 2^-52) + 2^-53: the tie goes to the even neighbour 1 + 2^-51
+    assert orc.exact_sum(np.array([one + ulp, 2.0 ** -53])) == one + 2 * ulp
+    # below half an ulp: down, however many tiny addends leave it below
+    assert orc.exact_sum(np.array([one] + [2.0 ** -60] * 127)) == one
+    assert orc.exact_sum(np.array([one] + [2.0 ** -60] * 129)) == one + ulp
+    # subnormal and overflow-edge sums are exact
+    assert orc.exact_sum(np.array([tiny] * 3)) == 3 * tiny
+    big = np.finfo(np.float64).max / 2
+    assert orc.exact_sum(np.array([big, big])) == np.finfo(np.float64).max
+    assert orc.exact_sum(np.zeros(5)) == 0.0
+    with pytest.raises(ValueError):
+        orc.exact_sum(np.array([1.0, -1.0]))
+
+
+def test_exact_sum_is_order_free(orc):
+    """Random orders of an array whose left-to-right binary64 sums differ
+    give one exactly rounded sum."""
+    import math
+    rng = np.random.default_rng(72)
+    x = np.concatenate([[1.0], np.full(300, 2.0 ** -54), rng.random(50) * 1e-3])
+    seen = set()
+    for _ in range(20):
+        p = rng.permutation(x)
+        acc = 0.0
+        for v in p:
+            acc += v
+        seen.add(acc)
+        assert orc.exact_sum(p) == math.fsum(x)
+    assert len(seen) > 1
 
 
 # ------------------------------------------- squared-ReLU gated FFN glue
@@ -655,3 +778,54 @@ def test_ffn_eps_dominates_tiny_activations(orc):
     q, s, qs, v = orc.ffn_act_quant(-np.abs(g), u, None, 1e-5)
     assert not v.any() and not q.any() and qs[0] == 0
     assert s[0] == np.float32(127.0 / 1e-5)
+
+
+def test_ffn_norm_factor_from_exact_sum(orc):
+    """The factor is fp32(1 / sqrt(S / F + eps)) with S the exactly rounded
+    sum of the (exact) squares: with S from math.fsum, v = (h * c) * gamma in
+    fp32 must equal the oracle's v bit for bit."""
+    import math
+    rng = np.random.default_rng(73)
+    N, F = 4, 640
+    g = (rng.standard_normal((N, F)) * np.exp2(rng.integers(-12, 3, (N, F)))).astype(np.float32)
+    u = rng.standard_normal((N, F)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, F).astype(np.float32)
+    for eps in (1e-5, 1e-6):
+        _, _, _, v = orc.ffn_act_quant(g, u, gamma, eps)
+        for n in range(N):
+            r = np.maximum(g[n], np.float32(0))
+            h = (r * r) * u[n]
+            S = math.fsum(h.astype(np.float64) ** 2)
+            c = np.float32(1.0 / math.sqrt(S / F + float(np.float32(eps))))
+            np.testing.assert_array_equal(v[n].view(np.uint32), ((h * c) * gamma).view(np.uint32))
+
+
+def test_ffn_is_channel_order_free(orc):
+    """Permuting the channels of g, u and gamma permutes v and the codes and
+    leaves s and the code sum unchanged, bit for bit (the sub-norm's sum has
+    no order)."""
+    rng = np.random.default_rng(74)
+    N, F = 3, 6912
+    g = (rng.standard_normal((N, F)) * np.exp2(rng.integers(-20, 4, (N, F)))).astype(np.float32)
+    u = rng.standard_normal((N, F)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, F).astype(np.float32)
+    q, s, qs, v = orc.ffn_act_quant(g, u, gamma, 1e-6)
+    p = rng.permutation(F)
+    q2, s2, qs2, v2 = orc.ffn_act_quant(np.ascontiguousarray(g[:, p]), np.ascontiguousarray(u[:, p]),
+                                        np.ascontiguousarray(gamma[p]), 1e-6)
+    np.testing.assert_array_equal(v2.view(np.uint32), v[:, p].view(np.uint32))
+    np.testing.assert_array_equal(q2, q[:, p])
+    np.testing.assert_array_equal(s2.view(np.uint32), s.view(np.uint32))
+    np.testing.assert_array_equal(qs2, qs)
+
+
+def test_ffn_factor_takes_the_exact_sum(orc):
+    """A token (tests/ffn_cases.py) whose left-to-right binary64 sum of
+    squares drops one ulp that the exact sum keeps, at a point where that ulp
+    changes the fp32 factor: the oracle's v follows the exact sum."""
+    import ffn_cases
+    g, u, eps, c_exact, c_ltr = ffn_cases.order_sensitive_token()
+    assert c_exact != c_ltr
+    q, s, qs, v = orc.ffn_act_quant(g, u, None, eps)
+    assert v[0, 0] == np.float32(11.0) * c_exact
+    assert v[0, 0] != np.float32(11.0) * c_ltr
