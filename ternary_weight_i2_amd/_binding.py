@@ -1,8 +1,10 @@
 """ctypes binding of libbitnet_i2s.so (C ABI in include/bitnet_i2s.h).
 
-Argument marshalling only: each function checks dtype/device/contiguity of
-its torch tensors, passes ``data_ptr()`` and the current HIP stream, and
-raises ``BitnetError`` on a non-zero status.  Every step of the computation
+Argument marshalling only: each function checks the dtype, shape, device
+and contiguity of every torch tensor it is given (so a wrong K or a short
+output buffer is refused on the host, never read or written out of bounds),
+passes ``data_ptr()`` and the current HIP stream, and raises ``BitnetError``
+on a non-zero status.  Every step of the computation
 runs in the library's HIP kernels; nothing here computes a result.
 """
 from __future__ import annotations
@@ -104,6 +106,49 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _expect(t, name, dtype, shape, device=None):
+    """Refuse a tensor of the wrong dtype, shape or device before any launch."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _expect_tokens(xq, x_scale, x_sum):
+    """Quantised tokens xq[N][K] int8 with s[N] fp32 and sum[N] int32 -> (N, K)."""
+    import torch
+    if xq is None or xq.dim() != 2:
+        raise ValueError("xq must be a 2-D [N][K] tensor")
+    N, K = xq.shape
+    _expect(xq, "xq", torch.int8, (N, K))
+    _expect(x_scale, "x_scale", torch.float32, (N,), xq.device)
+    _expect(x_sum, "x_sum", torch.int32, (N,), xq.device)
+    return N, K
+
+
+def _expect_packed(P, K, device, name="packed"):
+    """I2_S weights [M][K/4] uint8 for reduction length K -> M."""
+    import torch
+    if P is None or P.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [M][K/4] tensor")
+    if K % 4:
+        raise ValueError(f"K={K} is not a multiple of 4")
+    _expect(P, name, torch.uint8, (P.shape[0], K // 4), device)
+    return P.shape[0]
+
+
+def _expect_outputs(dot, y, N, M, device, name=""):
+    import torch
+    if dot is not None:
+        _expect(dot, f"{name}dot", torch.int32, (N, M), device)
+    if y is not None:
+        _expect(y, f"{name}y", torch.float32, (N, M), device)
+
+
 def abi_version() -> int:
     return load().bitnet_abi_version()
 
@@ -114,7 +159,9 @@ def pack(w):
     if w.dtype != torch.int8 or w.dim() != 2:
         raise TypeError("w must be a 2-D int8 tensor")
     M, K = w.shape
-    out = torch.empty((M, K // 4 if K % 4 == 0 else 0), dtype=torch.uint8, device=w.device)
+    if K % 4:
+        raise ValueError(f"K={K} is not a multiple of 4")
+    out = torch.empty((M, K // 4), dtype=torch.uint8, device=w.device)
     _check(load().bitnet_pack_i2s(_ptr(w), M, K, _ptr(out), _stream(w)))
     return out
 
@@ -129,8 +176,11 @@ def absmean_pack(w, out=None):
     if dt is None:
         raise TypeError("w must be float32 or bfloat16")
     M, K = w.shape
-    packed = out if out is not None else torch.empty((M, K // 4 if K % 4 == 0 else 0),
-                                                     dtype=torch.uint8, device=w.device)
+    if K % 4:
+        raise ValueError(f"K={K} is not a multiple of 4")
+    packed = out if out is not None else torch.empty((M, K // 4), dtype=torch.uint8,
+                                                     device=w.device)
+    _expect(packed, "out", torch.uint8, (M, K // 4), w.device)
     alpha = ctypes.c_float(0.0)
     _check(load().bitnet_absmean_i2s(_ptr(w), dt, M, K, _ptr(packed), ctypes.byref(alpha),
                                      _stream(w)))
@@ -144,8 +194,11 @@ def pack_f32(w, out=None):
     if w.dtype != torch.float32 or w.dim() != 2:
         raise TypeError("w must be a 2-D float32 tensor")
     M, K = w.shape
-    packed = out if out is not None else torch.empty((M, K // 4 if K % 4 == 0 else 0),
-                                                     dtype=torch.uint8, device=w.device)
+    if K % 4:
+        raise ValueError(f"K={K} is not a multiple of 4")
+    packed = out if out is not None else torch.empty((M, K // 4), dtype=torch.uint8,
+                                                     device=w.device)
+    _expect(packed, "out", torch.uint8, (M, K // 4), w.device)
     wmax = ctypes.c_float(0.0)
     _check(load().bitnet_pack_i2s_f32(_ptr(w), M, K, _ptr(packed), ctypes.byref(wmax),
                                       _stream(w)))
@@ -167,17 +220,21 @@ def quant_act(x, out=None):
         xs = torch.empty((N,), dtype=torch.int32, device=x.device)
     else:
         xq, s, xs = out
+        _expect(xq, "xq", torch.int8, (N, K), x.device)
+        _expect(s, "x_scale", torch.float32, (N,), x.device)
+        _expect(xs, "x_sum", torch.int32, (N,), x.device)
     _check(load().bitnet_quant_act_i8(_ptr(x), dt, N, K, _ptr(xq), _ptr(s),
                                       _ptr(xs), _stream(x)))
     return xq, s, xs
 
 
-def _matmul(fn, packed, w_scale, K, xq, x_scale, x_sum, want_dot, want_y, out):
+def _matmul(fn, packed, w_scale, xq, x_scale, x_sum, want_dot, want_y, out):
     import torch
-    M = packed.shape[0]
-    N = xq.shape[0]
+    N, K = _expect_tokens(xq, x_scale, x_sum)
+    M = _expect_packed(packed, K, xq.device)
     if out is not None:
         dot, y = out
+        _expect_outputs(dot, y, N, M, xq.device)
     else:
         dot = torch.empty((N, M), dtype=torch.int32, device=xq.device) if want_dot else None
         y = torch.empty((N, M), dtype=torch.float32, device=xq.device) if want_y else None
@@ -188,29 +245,34 @@ def _matmul(fn, packed, w_scale, K, xq, x_scale, x_sum, want_dot, want_y, out):
 
 def gemv(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     """Decode matmul (1..64 tokens) -> (int32 dot[N][M] | None, fp32 y[N][M] | None)."""
-    K = xq.shape[1]
-    return _matmul(load().bitnet_gemv_i2s_i8, packed, w_scale, K, xq, x_scale,
-                   x_sum, want_dot, want_y, out)
+    return _matmul(load().bitnet_gemv_i2s_i8, packed, w_scale, xq, x_scale, x_sum,
+                   want_dot, want_y, out)
 
 
 def gemv_lut(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     """Decode matmul by table lookup (K <= 8192) -> (dot | None, y | None),
     the same values as gemv."""
-    K = xq.shape[1]
-    return _matmul(load().bitnet_gemv_i2s_lut, packed, w_scale, K, xq, x_scale,
-                   x_sum, want_dot, want_y, out)
+    return _matmul(load().bitnet_gemv_i2s_lut, packed, w_scale, xq, x_scale, x_sum,
+                   want_dot, want_y, out)
 
 
 def gemm(packed, w_scale, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     """Prefill matmul (any token count, int8 MFMA) -> (dot | None, y | None)."""
-    K = xq.shape[1]
-    return _matmul(load().bitnet_gemm_i2s_i8, packed, w_scale, K, xq, x_scale,
-                   x_sum, want_dot, want_y, out)
+    return _matmul(load().bitnet_gemm_i2s_i8, packed, w_scale, xq, x_scale, x_sum,
+                   want_dot, want_y, out)
 
 
-def _mats_out(mats, N, device, want_dot, want_y, out):
+def _mats_out(mats, N, K, device, want_dot, want_y, out):
     import torch
+    if not 1 <= len(mats) <= MAX_GROUP:
+        raise ValueError(f"{len(mats)} matrices; a call takes 1..{MAX_GROUP}")
+    for i, (P, _) in enumerate(mats):
+        _expect_packed(P, K, device, f"mats[{i}] packed")
     if out is not None:
+        if len(out) != len(mats):
+            raise ValueError("out must hold one (dot, y) pair per matrix")
+        for i, ((P, _), (d, y)) in enumerate(zip(mats, out)):
+            _expect_outputs(d, y, N, P.shape[0], device, f"out[{i}] ")
         return out
     res = []
     for P, _ in mats:
@@ -230,8 +292,8 @@ def _mat_array(mats, out):
 def gemm_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     """Prefill matmul of every (packed, w_scale) in ``mats`` by the same
     quantised tokens, one MFMA launch -> [(dot | None, y | None) per matrix]."""
-    N, K = xq.shape
-    out = _mats_out(mats, N, xq.device, want_dot, want_y, out)
+    N, K = _expect_tokens(xq, x_scale, x_sum)
+    out = _mats_out(mats, N, K, xq.device, want_dot, want_y, out)
     _check(load().bitnet_gemm_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
                                            _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
     return out
@@ -240,8 +302,8 @@ def gemm_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
 def gemv_group(mats, xq, x_scale, x_sum, want_dot=True, want_y=True, out=None):
     """Decode matmul (N <= 64 quantised tokens) of every (packed, w_scale) in
     ``mats`` -> [(dot | None, y | None) per matrix]."""
-    N, K = xq.shape
-    out = _mats_out(mats, N, xq.device, want_dot, want_y, out)
+    N, K = _expect_tokens(xq, x_scale, x_sum)
+    out = _mats_out(mats, N, K, xq.device, want_dot, want_y, out)
     _check(load().bitnet_gemv_i2s_i8_group(_mat_array(mats, out), len(mats), K, _ptr(xq),
                                            _ptr(x_scale), _ptr(x_sum), N, _stream(xq)))
     return out
@@ -254,11 +316,18 @@ def ffn_act_quant(g, u, gamma=None, eps=1e-5, out=None):
     if g.dtype != torch.float32 or u.dtype != torch.float32 or g.shape != u.shape or g.dim() != 2:
         raise TypeError("g and u must be float32 tensors of the same 2-D shape")
     N, F = g.shape
+    if u.device != g.device:
+        raise ValueError("g and u must be on the same device")
+    if gamma is not None:
+        _expect(gamma, "gamma", torch.float32, (F,), g.device)
     if out is None:
         out = (torch.empty((N, F), dtype=torch.int8, device=g.device),
                torch.empty((N,), dtype=torch.float32, device=g.device),
                torch.empty((N,), dtype=torch.int32, device=g.device))
     xq, xs, xsum = out
+    _expect(xq, "xq", torch.int8, (N, F), g.device)
+    _expect(xs, "x_scale", torch.float32, (N,), g.device)
+    _expect(xsum, "x_sum", torch.int32, (N,), g.device)
     _check(load().bitnet_ffn_act_quant_i8(_ptr(g), _ptr(u), _ptr(gamma), float(eps), N, F,
                                           _ptr(xq), _ptr(xs), _ptr(xsum), _stream(g)))
     return xq, xs, xsum
@@ -293,12 +362,16 @@ def linear(x, mats, want_dot=True, want_y=True, out=None, qout=None):
     if dt is None:
         raise TypeError("x must be float32 or bfloat16")
     N, K = x.shape
-    out = _mats_out(mats, N, x.device, want_dot, want_y, out)
+    out = _mats_out(mats, N, K, x.device, want_dot, want_y, out)
     if qout is None and N > LINEAR_FUSED_MAX_N:
         qout = (torch.empty((N, K), dtype=torch.int8, device=x.device),
                 torch.empty((N,), dtype=torch.float32, device=x.device),
                 torch.empty((N,), dtype=torch.int32, device=x.device))
     xq, xs, xsum = qout if qout is not None else (None, None, None)
+    if qout is not None:
+        _expect(xq, "qout xq", torch.int8, (N, K), x.device)
+        _expect(xs, "qout x_scale", torch.float32, (N,), x.device)
+        _expect(xsum, "qout x_sum", torch.int32, (N,), x.device)
     _check(load().bitnet_linear_i2s(_ptr(x), dt, N, K, _mat_array(mats, out), len(mats),
                                     _ptr(xq), _ptr(xs), _ptr(xsum), _stream(x)))
     return out, qout

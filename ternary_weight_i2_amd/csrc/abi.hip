@@ -73,7 +73,8 @@ int pack_counter(int dev, unsigned **out) {
 // per device, its address looked up once per device, and the calls that use
 // it serialised by g_pack_mu and synchronised before they return.
 struct ConvScratch {
-    double partial[bitnet::kConvPartials];
+    uint32_t digits[bitnet::kConvPartials * bitnet::kConvDigits];   // AbsMean partial sums
+    double partial[bitnet::kConvPartials];                          // max|w| per workgroup
     float alpha;
     unsigned bad;
     float wmax;
@@ -164,6 +165,8 @@ BITNET_API int bitnet_absmean_i2s(const void *w, int dtype, int64_t M, int64_t K
         return fail(BITNET_E_DTYPE, "%s: unknown dtype %d", fn, dtype);
     if (M < 1) return fail(BITNET_E_SHAPE, "%s: M=%lld, need at least one row", fn, (long long)M);
     if (int s = check_k(fn, K)) return s;
+    if (M > (1LL << 40) / K)
+        return fail(BITNET_E_SHAPE, "%s: M*K exceeds 2^40 weights", fn);
     if (!w || !packed || !alpha) return fail(BITNET_E_NULL, "%s: w, packed and alpha are required", fn);
     if (!aligned(w, 16) || !aligned(packed, 16))
         return fail(BITNET_E_ALIGN, "%s: w and packed must be 16-byte aligned", fn);
@@ -173,7 +176,7 @@ BITNET_API int bitnet_absmean_i2s(const void *w, int dtype, int64_t M, int64_t K
     if (int s = conv_scratch(fn, &sc)) return s;
     hipError_t e = hipMemsetAsync(&sc->bad, 0, sizeof(unsigned), st);
     const int bf16 = dtype == BITNET_BF16;
-    if (e == hipSuccess) e = bitnet::launch_absmean_alpha(w, bf16, M * K, sc->partial, &sc->alpha, st);
+    if (e == hipSuccess) e = bitnet::launch_absmean_alpha(w, bf16, M * K, sc->digits, &sc->alpha, st);
     if (e == hipSuccess)
         e = bitnet::launch_ternary_pack(w, bf16, 0, M, K, &sc->alpha, packed, &sc->bad, nullptr,
                                         nullptr, st);

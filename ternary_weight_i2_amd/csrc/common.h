@@ -186,8 +186,9 @@ hipError_t launch_ffn_act_quant(const float *g, const float *u, const float *gam
                                 hipStream_t st);
 
 // One-time weight conversion (AbsMean ternariser, sign/threshold packer).
-constexpr int kConvPartials = 1024;   // partial sums of the AbsMean reduction
-hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, double *partial,
+constexpr int kConvPartials = 1024;   // workgroups of the AbsMean and max reductions
+constexpr int kConvDigits = 12;       // 32-bit digits of one exact partial sum of |w|
+hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, uint32_t *partial,
                                 float *alpha, hipStream_t st);
 hipError_t launch_ternary_pack(const void *w, int bf16, int mode, int64_t M, int64_t K,
                                const float *alpha, uint8_t *packed, unsigned *bad,

@@ -7,17 +7,20 @@
 // positive ones code 2, negative ones code 0), §1-1 (code table); [P4]
 // "bitnet.rs", "Mathematical Foundation" (AbsMean formula).
 //
-// AbsMean in two deterministic passes over the tensor: a fixed grid of
-// workgroups each sums |w| of a fixed, strided share in binary64
-// (partial[]), then one workgroup adds the partials in a fixed order and
-// rounds the mean once to fp32.  The same input therefore always gives the
-// same alpha.  The pack pass then reads alpha from device memory, so the
-// three launches need no host round trip.
+// AbsMean: the sum of |w| is taken exactly (exact_sum.h: every fp32
+// magnitude added into 32-bit digits that span the whole fp32 range), then
+// rounded once to binary64, divided by n in binary64 and rounded to fp32, so
+// alpha does not depend on how the sum is split.  A grid of workgroups each
+// adds a strided share and writes its digits (partial[]); one workgroup adds
+// the partials and forms alpha.  The pack pass then reads alpha from device
+// memory, so the three launches need no host round trip.
 #include "common.h"
+#include "exact_sum.h"
 
 namespace bitnet {
 
 constexpr int kConvThreads = 256;
+static_assert(kConvDigits == kMagNorm, "digits of one AbsMean partial sum");
 
 // 4 consecutive weights, widened to fp32 (16 bytes of fp32 or 8 of bf16)
 template <int BF16>
@@ -34,49 +37,71 @@ __device__ __forceinline__ void load4(const void *w, int64_t g, float *v) {
     }
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
+__device__ __forceinline__ uint64_t wave_sum_u64c(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
-// Pass 1: partial[b] = sum of |w| over groups of 4 weights g = b*256 + t,
-// g += gridDim*256 (binary64; order fixed by the grid).
+// Pass 1: the digits of sum |w| over groups of 4 weights g = b*256 + t,
+// g += gridDim*256, normalised into partial[b][0..kMagNorm).  Each digit of a
+// workgroup stays below 2^32 * (weights of the workgroup) < 2^64.
 template <int BF16>
 __global__ __launch_bounds__(kConvThreads) void absmean_partial_kernel(
-    const void *__restrict__ w, int64_t n4, double *__restrict__ partial) {
-    __shared__ double red[kConvThreads / 64];
-    double acc = 0.0;
+    const void *__restrict__ w, int64_t n4, uint32_t *__restrict__ partial) {
+    __shared__ uint64_t red[kConvThreads / 64][kMagDigits];
+    uint64_t d[kMagDigits];
+#pragma unroll
+    for (int i = 0; i < kMagDigits; ++i) d[i] = 0;
     for (int64_t g = (int64_t)blockIdx.x * kConvThreads + threadIdx.x; g < n4;
          g += (int64_t)gridDim.x * kConvThreads) {
         float v[4];
         load4<BF16>(w, g, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc += fabs((double)v[e]);
+        for (int e = 0; e < 4; ++e) mag_add(d, v[e]);
     }
-    acc = wave_sum_f64(acc);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+#pragma unroll
+    for (int i = 0; i < kMagDigits; ++i) d[i] = wave_sum_u64c(d[i]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int i = 0; i < kMagDigits; ++i) red[threadIdx.x >> 6][i] = d[i];
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < kConvThreads / 64; ++i) s += red[i];
-        partial[blockIdx.x] = s;
+        uint64_t t[kMagDigits];
+        for (int i = 0; i < kMagDigits; ++i) {
+            t[i] = 0;
+            for (int wv = 0; wv < kConvThreads / 64; ++wv) t[i] += red[wv][i];
+        }
+        mag_normalise(t, kMagDigits, partial + (int64_t)blockIdx.x * kMagNorm);
     }
 }
 
-// Pass 2 (one workgroup): alpha = max(fp32(sum / n), 1e-5).
+// Pass 2 (one workgroup, a thread per partial): the exact total, rounded once
+// to binary64; alpha = max(fp32(sum / n), 1e-5).
 __global__ __launch_bounds__(1024) void absmean_final_kernel(
-    const double *__restrict__ partial, int nparts, int64_t n, float *__restrict__ alpha) {
-    __shared__ double red[16];
-    double v = (int)threadIdx.x < nparts ? partial[threadIdx.x] : 0.0;
-    v = wave_sum_f64(v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    const uint32_t *__restrict__ partial, int nparts, int64_t n, float *__restrict__ alpha) {
+    __shared__ uint64_t red[16][kMagNorm];
+    uint64_t d[kMagNorm];
+#pragma unroll
+    for (int i = 0; i < kMagNorm; ++i)
+        d[i] = (int)threadIdx.x < nparts ? partial[(int64_t)threadIdx.x * kMagNorm + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kMagNorm; ++i) d[i] = wave_sum_u64c(d[i]);
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int i = 0; i < kMagNorm; ++i) red[threadIdx.x >> 6][i] = d[i];
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += red[i];
+        uint64_t t[kMagNorm];
+        for (int i = 0; i < kMagNorm; ++i) {
+            t[i] = 0;
+            for (int wv = 0; wv < 16; ++wv) t[i] += red[wv][i];
+        }
+        uint32_t nd[kMagNorm];
+        mag_normalise(t, kMagNorm, nd);
+        const double s = mag_round(nd);
         const float a = (float)(s / (double)n);
         *alpha = a > 1e-5f ? a : 1e-5f;
     }
@@ -158,7 +183,7 @@ __global__ __launch_bounds__(1024) void max_final_kernel(const double *__restric
     }
 }
 
-hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, double *partial,
+hipError_t launch_absmean_alpha(const void *w, int bf16, int64_t n, uint32_t *partial,
                                 float *alpha, hipStream_t st) {
     const int64_t n4 = n / 4;
     int64_t parts = (n4 + kConvThreads * 8 - 1) / (kConvThreads * 8);   // >= 8 groups per thread

@@ -1,0 +1,225 @@
+// exact_sum.h -- exactly rounded binary64 sums of non-negative values whose
+// bits are known exactly (squares of fp32 values; magnitudes of fp32 values),
+// for the FFN sub-norm and the AbsMean scale.  The result is the exact sum
+// rounded once to nearest-even, so it depends on no summation order and a
+// reduction may be split across lanes, waves and workgroups freely.
+//
+// Pages: [P4] "bitnet.rs", "Forward Pass" (ffn_sub_norm of the squared-ReLU
+// gated product) and "Mathematical Foundation" (AbsMean, mean |W|); [P1]
+// "BitNet 딥다이브" §6-2 (AbsMean).  Neither fixes a summation order; every
+// h^2 of an fp32 h and every |w| of an fp32 w is exact in binary64, so the
+// exact sum is well defined and taken here.
+//
+// Two schemes:
+//  * Window sums (squares).  An fp32 h = m * 2^(e) with m < 2^24 gives
+//    h^2 = v * 2^(P - 298), v = m^2 < 2^48, P in [0, 506].  With T the top bit
+//    position of the largest square of a token, level 1 keeps every square's
+//    bits at positions >= b1 = T - kWin exactly in a 128-bit integer (unit
+//    2^b1) and counts the squares that have bits below b1.  If the count
+//    cannot carry into the round bit, the level-1 integer decides the
+//    rounding; otherwise further levels add the next kWin bits of every
+//    square into an exact big integer until no square has bits left below.
+//  * Digit sums (magnitudes).  |w| = m * 2^P' in units of 2^-149, P' in
+//    [0, 253], m < 2^24: added into nine 32-bit digits held in 64-bit lanes
+//    (carry-save; no carries while accumulating), which covers every finite
+//    fp32 with no window and no second level.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+constexpr int kWin = 112;        // bits per window level (sums of 2^15 terms fit in 128)
+constexpr int kBigDigits = 32;   // 32-bit digits of the slow path's exact integer
+
+struct U128 {
+    uint64_t lo, hi;
+};
+
+__host__ __device__ __forceinline__ void add128(U128 &a, const U128 &b) {
+    const uint64_t lo = a.lo + b.lo;
+    a.hi += b.hi + (lo < a.lo ? 1u : 0u);
+    a.lo = lo;
+}
+
+// h -> (v, P): h^2 = v * 2^(P - 298) exactly (v = 0 for h = 0).
+__host__ __device__ __forceinline__ void square_parts(float h, uint64_t &v, int &P) {
+    uint32_t bits;
+    __builtin_memcpy(&bits, &h, 4);
+    bits &= 0x7fffffffu;
+    const uint32_t E = bits >> 23, mant = bits & 0x7fffffu;
+    const uint64_t m = E ? (mant | 0x800000u) : mant;
+    v = m * m;
+    P = E ? 2 * (int)E - 2 : 0;
+}
+
+// Position (in units of 2^-298) of the top bit of v * 2^P, v > 0.
+__host__ __device__ __forceinline__ int top_position(uint64_t v, int P) {
+    return P + 63 - __builtin_clzll(v);
+}
+
+// Bits [b, b + kWin) of x = v * 2^P (all bits >= b when !masked), as an
+// integer in units of 2^b; *rem is set when x has bits below b.
+__host__ __device__ __forceinline__ U128 window_bits(uint64_t v, int P, int b, bool masked,
+                                                     bool *rem) {
+    U128 r{0, 0};
+    const int d = P - b;
+    if (d >= 0) {
+        *rem = false;
+        if (d < 64) {
+            r.lo = v << d;
+            r.hi = d ? v >> (64 - d) : 0;
+        } else if (d < 128) {
+            r.hi = v << (d - 64);
+        }
+        if (masked) {
+            if (d >= kWin) r = U128{0, 0};
+            else r.hi &= (1ull << (kWin - 64)) - 1;
+        }
+    } else {
+        const int s = -d;
+        if (s < 64) {
+            r.lo = v >> s;
+            *rem = (v & ((1ull << s) - 1)) != 0;
+        } else {
+            *rem = v != 0;
+        }
+    }
+    return r;
+}
+
+__host__ __device__ __forceinline__ int top_bit128(const U128 &a) {
+    return a.hi ? 127 - __builtin_clzll(a.hi) : 63 - __builtin_clzll(a.lo);
+}
+__host__ __device__ __forceinline__ uint64_t shr128(const U128 &a, int s) {   // low 64 bits of a >> s
+    if (s == 0) return a.lo;
+    if (s < 64) return (a.lo >> s) | (a.hi << (64 - s));
+    return a.hi >> (s - 64);
+}
+__host__ __device__ __forceinline__ bool low_bits_zero128(const U128 &a, int s) {   // a mod 2^s == 0
+    if (s <= 0) return true;
+    if (s < 64) return (a.lo & ((1ull << s) - 1)) == 0;
+    if (a.lo) return false;
+    return s == 64 || (a.hi & ((1ull << (s - 64)) - 1)) == 0;
+}
+// a mod 2^s + c > 2^s ?  (0 < s < 128, c >= 0 small)
+__host__ __device__ __forceinline__ bool may_carry128(const U128 &a, int s, uint64_t c) {
+    if (c == 0) return false;
+    // room = 2^s - (a mod 2^s); carry possible when c > room
+    if (s < 64) {
+        const uint64_t low = a.lo & ((1ull << s) - 1);
+        return c > (1ull << s) - low;
+    }
+    const uint64_t hmask = s == 64 ? 0 : (1ull << (s - 64)) - 1;
+    const uint64_t lh = a.hi & hmask;
+    if (lh != hmask) return false;   // room >= 2^64 > c
+    // high part of the low bits all ones: room = 2^64 - a.lo
+    return a.lo != 0 && c > (~a.lo) + 1;
+}
+
+// Level 1: A = sum of the window integers (unit 2^(b - 298)), cnt = number of
+// squares with bits below b.  If the rounding of the exact sum is decided,
+// writes it to *ss and returns true.  A >= 2^kWin (the largest square alone).
+__host__ __device__ __forceinline__ bool round_level1(const U128 &A, uint64_t cnt, int b,
+                                                      double *ss) {
+    const int t = top_bit128(A);
+    const int r = t - 53;                     // round-bit index (>= kWin - 53)
+    if (may_carry128(A, r, cnt)) return false;
+    uint64_t keep = shr128(A, r + 1);         // 53 bits
+    const bool rb = (shr128(A, r) & 1u) != 0;
+    const bool sticky = cnt != 0 || !low_bits_zero128(A, r);
+    if (rb && (sticky || (keep & 1u))) ++keep;
+    *ss = __builtin_ldexp((double)keep, r + 1 + b - 298);
+    return true;
+}
+
+// ---- slow path: an exact big integer, 32-bit digits, least significant first
+// big = big * 2^kWin + a
+__host__ __device__ __forceinline__ void big_shift_add(uint32_t *big, const U128 &a) {
+    const int ds = kWin / 32, bs = kWin % 32;   // 3 digits and 16 bits
+    for (int i = kBigDigits - 1; i >= 0; --i) {
+        const int j = i - ds;
+        uint64_t v = 0;
+        if (j >= 0) v = (uint64_t)big[j] << bs;
+        if (j - 1 >= 0 && bs) v |= (uint64_t)big[j - 1] >> (32 - bs);
+        big[i] = (uint32_t)v;
+    }
+    const uint32_t add[4] = {(uint32_t)a.lo, (uint32_t)(a.lo >> 32), (uint32_t)a.hi,
+                             (uint32_t)(a.hi >> 32)};
+    uint64_t carry = 0;
+    for (int i = 0; i < kBigDigits; ++i) {
+        const uint64_t s = (uint64_t)big[i] + (i < 4 ? add[i] : 0u) + carry;
+        big[i] = (uint32_t)s;
+        carry = s >> 32;
+    }
+}
+__host__ __device__ __forceinline__ int big_bit(const uint32_t *big, int i) {
+    return (int)((big[i >> 5] >> (i & 31)) & 1u);
+}
+// The exact integer big (unit 2^(b - 298)) rounded once to binary64.
+__host__ __device__ __forceinline__ double big_round(const uint32_t *big, int b) {
+    int top = -1;
+    for (int i = kBigDigits - 1; i >= 0 && top < 0; --i)
+        if (big[i]) top = 32 * i + 31 - __builtin_clz(big[i]);
+    if (top < 0) return 0.0;
+    uint64_t keep = 0;
+    const int lo = top - 52;
+    for (int i = top; i >= lo && i >= 0; --i) keep = 2 * keep + (uint64_t)big_bit(big, i);
+    if (lo <= 0) return __builtin_ldexp((double)keep, b - 298);   // at most 53 bits: exact
+    const int rb = big_bit(big, lo - 1);
+    int sticky = 0;
+    for (int i = lo - 2; i >= 0 && !sticky; --i) sticky = big_bit(big, i);
+    if (rb && (sticky || (keep & 1u))) ++keep;
+    return __builtin_ldexp((double)keep, lo + b - 298);
+}
+
+// ---- digit sums of fp32 magnitudes (AbsMean) ----
+constexpr int kMagDigits = 9;     // 288 bits >= 24 + 253
+constexpr int kMagNorm = 12;      // normalised digits of a (workgroup or total) sum
+
+// |w| into the carry-save digits d[0..8] (units 2^-149); non-finite ignored.
+__host__ __device__ __forceinline__ void mag_add(uint64_t *d, float w) {
+    uint32_t bits;
+    __builtin_memcpy(&bits, &w, 4);
+    bits &= 0x7fffffffu;
+    const uint32_t E = bits >> 23;
+    if (E == 0xffu) return;
+    const uint64_t m = E ? ((bits & 0x7fffffu) | 0x800000u) : (bits & 0x7fffffu);
+    const int P = E ? (int)E - 1 : 0;
+    const int q = P >> 5;
+    const uint64_t t = m << (P & 31);
+    const uint64_t lo = t & 0xffffffffu, hi = t >> 32;
+#pragma unroll
+    for (int i = 0; i < kMagDigits; ++i) d[i] += (q == i ? lo : 0) + (q + 1 == i ? hi : 0);
+}
+
+// Carry-save digits (each < 2^64) -> normalised 32-bit digits.
+__host__ __device__ __forceinline__ void mag_normalise(const uint64_t *d, int nd, uint32_t *out) {
+    uint64_t carry = 0;
+    for (int i = 0; i < kMagNorm; ++i) {
+        const uint64_t x = (i < nd ? d[i] : 0);
+        const uint64_t lo = (x & 0xffffffffu) + (carry & 0xffffffffu);
+        out[i] = (uint32_t)lo;
+        carry = (x >> 32) + (carry >> 32) + (lo >> 32);
+    }
+}
+
+// Normalised digits (units 2^-149) rounded once to binary64.
+__host__ __device__ __forceinline__ double mag_round(const uint32_t *n) {
+    int top = -1;
+    for (int i = kMagNorm - 1; i >= 0 && top < 0; --i)
+        if (n[i]) top = 32 * i + 31 - __builtin_clz(n[i]);
+    if (top < 0) return 0.0;
+    auto bit = [&](int i) { return (int)((n[i >> 5] >> (i & 31)) & 1u); };
+    uint64_t keep = 0;
+    const int lo = top - 52;
+    for (int i = top; i >= lo && i >= 0; --i) keep = 2 * keep + (uint64_t)bit(i);
+    if (lo <= 0) return __builtin_ldexp((double)keep, -149);
+    const int rb = bit(lo - 1);
+    int sticky = 0;
+    for (int i = lo - 2; i >= 0 && !sticky; --i) sticky = bit(i);
+    if (rb && (sticky || (keep & 1u))) ++keep;
+    return __builtin_ldexp((double)keep, lo - 149);
+}
+
+}  // namespace bitnet

@@ -5,139 +5,230 @@
 // ffn_sub_norm(sqrelu(gate(x)) * up(x)) and feeds it to down); [P1]
 // "BitNet 딥다이브" §4-5 (per-token absmax int8 activations).
 //
-// One workgroup per token.  Pass 1: each thread takes runs of 32 channels,
-// forms h = (relu(g)^2) * u in fp32, keeps h in LDS and sums h^2 over its run
-// in binary64 in index order (the squares of fp32 values are exact in
-// binary64).  One thread then adds the run sums in index order and forms the
-// factor c = fp32(1 / sqrt(sum / F + eps)); this fixed order makes the factor,
-// and so every int8 code, independent of the launch shape.  Pass 2: v =
-// (h * c) * gamma over the same runs (kept in LDS) and its absmax; pass 3: the
-// scale and the codes, with the same arithmetic as the stand-alone activation
-// quantiser.  Every pass works on whole 32-channel runs with 16-byte loads,
-// so a thread's loads are in flight together.
+// One workgroup per token, 512 threads on 16-byte pieces (four channels).
+// Pass 1 forms h = (relu(g)^2) * u in fp32, keeps it in LDS and finds max|h|.
+// The sub-norm's sum of squares is the exact sum rounded once to binary64
+// (exact_sum.h): every thread adds the bits of its squares that lie in a
+// 112-bit window below the largest square into a 128-bit integer and counts
+// the squares with bits below the window; the workgroup adds the integers and
+// counts, and one thread rounds -- or, when the count could carry into the
+// round bit, the workgroup adds further windows into an exact integer first.
+// c = fp32(1 / sqrt(sum / F + eps)).  Pass 2: v = (h * c) * gamma in place
+// and its absmax; pass 3: the scale and the codes with the activation
+// quantiser's arithmetic.
 #include "common.h"
+#include "exact_sum.h"
 
 namespace bitnet {
 
-constexpr int kFfnThreads = 256;
+constexpr int kFfnThreads = 512;
+constexpr int kFfnWaves = kFfnThreads / 64;
+constexpr int kFfnR = 4;   // 16-byte pieces per thread loaded together
+
+struct FfnShared {
+    uint64_t red[kFfnWaves][5];   // 32-bit digits of the window sums + count
+    float redf[kFfnWaves];
+    int redi[kFfnWaves];
+    uint32_t big[kBigDigits];
+    double ss;
+    float hmax;
+    float c;
+    int state;   // 0: sum decided, 1: more windows needed
+};
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Adds every thread's (a, cnt); thread 0 receives the totals.
+__device__ __forceinline__ void block_sum_window(const U128 &a, uint32_t cnt, FfnShared &sh,
+                                                 U128 *tot, uint64_t *tot_cnt) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint64_t d[5] = {a.lo & 0xffffffffu, a.lo >> 32, a.hi & 0xffffffffu, a.hi >> 32, cnt};
+#pragma unroll
+    for (int i = 0; i < 5; ++i) d[i] = wave_sum_u64(d[i]);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) sh.red[wv][i] = d[i];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t D[5] = {0, 0, 0, 0, 0};
+        for (int w = 0; w < kFfnWaves; ++w)
+#pragma unroll
+            for (int i = 0; i < 5; ++i) D[i] += sh.red[w][i];
+        // the digit sums are below 2^42; the exact total is below 2^128
+        U128 r{D[0], 0};
+        add128(r, U128{D[1] << 32, D[1] >> 32});
+        add128(r, U128{0, D[2]});
+        add128(r, U128{0, D[3] << 32});
+        *tot = r;
+        *tot_cnt = D[4];
+    }
+}
+
+// This thread's part of window level b: bits of its squares at positions
+// >= b (below b + kWin when masked), and how many squares have bits below b.
+__device__ __forceinline__ void window_pass(const float4 *hl, int nq, int b, bool masked,
+                                            U128 *acc, uint32_t *cnt) {
+    U128 a{0, 0};
+    uint32_t c = 0;
+    for (int q = threadIdx.x; q < nq; q += kFfnThreads) {
+        const float4 h4 = hl[q];
+        const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint64_t v;
+            int P;
+            square_parts(hv[e], v, P);
+            if (v) {
+                bool rem;
+                add128(a, window_bits(v, P, b, masked, &rem));
+                c += rem ? 1u : 0u;
+            }
+        }
+    }
+    *acc = a;
+    *cnt = c;
+}
 
 __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
     const float *__restrict__ g, const float *__restrict__ u, const float *__restrict__ gamma,
     float eps, int F, int8_t *__restrict__ xq, float *__restrict__ xs,
     int32_t *__restrict__ xsum) {
-    // h[F] in LDS column-major over the runs -- channel j of run r at
-    // j * nruns + r -- so the lanes of a wave (consecutive runs) hit
-    // consecutive banks; then the run sums (double)
-    extern __shared__ float hl[];
-    double *runs = reinterpret_cast<double *>(hl + F); // F is a multiple of 128: 8-byte aligned
-    __shared__ float c_tok, red_f[kFfnThreads / 64];
-    __shared__ int red_i[kFfnThreads / 64];
+    extern __shared__ float4 hl[];   // h (then v) of the token, F/4 pieces
+    __shared__ FfnShared sh;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nq = F >> 2;
     const int64_t row = (int64_t)blockIdx.x * F;
     const float4 *g4 = reinterpret_cast<const float4 *>(g + row);
     const float4 *u4 = reinterpret_cast<const float4 *>(u + row);
-    const int nruns = F / 32;
+    const float4 *gm4 = reinterpret_cast<const float4 *>(gamma);
 
-    // The gain of the thread's first run is loaded with g and u, so pass 2
-    // needs no second memory round trip when every run fits one thread
-    // (F <= 8192); further runs load theirs in pass 2.
-    float4 gm0[8];
+    // ---- pass 1: h and max|h|; the gain of the first batch loads alongside
+    float4 gm0[kFfnR];
+    float hmax = 0.0f;
+    for (int base = 0; base < nq; base += kFfnR * kFfnThreads) {
+        float4 gv[kFfnR], uv[kFfnR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        gm0[i] = gamma && tid < nruns ? reinterpret_cast<const float4 *>(gamma)[tid * 8 + i]
-                                      : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-
-    for (int r = tid; r < nruns; r += kFfnThreads) {
-        double part = 0.0;
+        for (int r = 0; r < kFfnR; ++r) {
+            const int q = min(base + tid + r * kFfnThreads, nq - 1);
+            gv[r] = g4[q];
+            uv[r] = u4[q];
+            if (base == 0) gm0[r] = gamma ? gm4[q] : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 gv = g4[r * 8 + i], uv = u4[r * 8 + i];
-            const float gg[4] = {gv.x, gv.y, gv.z, gv.w}, uu[4] = {uv.x, uv.y, uv.z, uv.w};
+        for (int r = 0; r < kFfnR; ++r) {
+            const int q = base + tid + r * kFfnThreads;
+            if (q < nq) {
+                const float gg[4] = {gv[r].x, gv[r].y, gv[r].z, gv[r].w};
+                const float uu[4] = {uv[r].x, uv[r].y, uv[r].z, uv[r].w};
+                float h[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float rl = gg[e] > 0.0f ? gg[e] : 0.0f;
-                const float h = (rl * rl) * uu[e];
-                hl[(i * 4 + e) * nruns + r] = h;
-                part += (double)h * (double)h;
+                for (int e = 0; e < 4; ++e) {
+                    const float rl = gg[e] > 0.0f ? gg[e] : 0.0f;
+                    h[e] = (rl * rl) * uu[e];
+                    hmax = fmaxf(hmax, fabsf(h[e]));
+                }
+                hl[q] = make_float4(h[0], h[1], h[2], h[3]);
             }
         }
-        runs[r] = part;
     }
+    hmax = wave_max_f32(hmax);
+    if (lane == 0) sh.redf[wv] = hmax;
     __syncthreads();
     if (tid == 0) {
-        // the run sums in index order; the LDS reads go out 32 at a time so
-        // the chain of adds does not wait on one read per step
-        double ss = 0.0;
-        int r = 0;
-        for (; r + 32 <= nruns; r += 32) {
-            double t[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) t[i] = runs[r + i];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) ss += t[i];
-        }
-        for (; r < nruns; ++r) ss += runs[r];
-        c_tok = (float)(1.0 / sqrt(ss / (double)F + (double)eps));
+        float m = sh.redf[0];
+        for (int w = 1; w < kFfnWaves; ++w) m = fmaxf(m, sh.redf[w]);
+        sh.hmax = m;
     }
     __syncthreads();
-    const float c = c_tok;
-    // Pass 2: v = (h * c) * gamma over the thread's own runs (16-byte loads of
-    // the gain, all eight of a run in flight), kept in LDS in place of h.
-    float amax = 0.0f;
-    for (int r = tid; r < nruns; r += kFfnThreads) {
-        float4 gm[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            gm[i] = r == tid ? gm0[i]
-                  : gamma    ? reinterpret_cast<const float4 *>(gamma)[r * 8 + i]
-                             : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float ga[4] = {gm[i].x, gm[i].y, gm[i].z, gm[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int k = (i * 4 + e) * nruns + r;
-                const float t = hl[k] * c;
-                const float v = gamma ? t * ga[e] : t;
-                hl[k] = v;
-                amax = fmaxf(amax, fabsf(v));
+
+    // ---- the exactly rounded sum of h^2
+    const float hm = sh.hmax;
+    if (hm == 0.0f) {
+        if (tid == 0) sh.ss = 0.0;
+    } else {
+        uint64_t vmax;
+        int Pmax;
+        square_parts(hm, vmax, Pmax);
+        const int T = top_position(vmax, Pmax);
+        U128 acc, A;
+        uint32_t cnt;
+        uint64_t C;
+        window_pass(hl, nq, T - kWin, false, &acc, &cnt);
+        block_sum_window(acc, cnt, sh, &A, &C);
+        if (tid == 0) {
+            double s;
+            if (round_level1(A, C, T - kWin, &s)) {
+                sh.ss = s;
+                sh.state = 0;
+            } else {
+                for (int i = 0; i < kBigDigits; ++i) sh.big[i] = 0;
+                big_shift_add(sh.big, A);
+                sh.state = 1;
             }
         }
+        __syncthreads();
+        // Rare: a carry into the round bit is possible.  Add the next windows
+        // of every square until no square has bits left below the window
+        // (at most five levels cover the whole range of squares of fp32).
+        for (int k = 2; k <= 8 && sh.state == 1; ++k) {
+            const int b = T - kWin * k;
+            window_pass(hl, nq, b, true, &acc, &cnt);
+            block_sum_window(acc, cnt, sh, &A, &C);
+            if (tid == 0) {
+                big_shift_add(sh.big, A);
+                if (C == 0) {
+                    sh.ss = big_round(sh.big, b);
+                    sh.state = 0;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (tid == 0) sh.c = (float)(1.0 / sqrt(sh.ss / (double)F + (double)eps));
+    __syncthreads();
+    const float c = sh.c;
+
+    // ---- pass 2: v = (h * c) * gamma in place, and its absmax
+    float amax = 0.0f;
+    for (int q = tid, r = 0; q < nq; q += kFfnThreads, ++r) {
+        const float4 gm = r < kFfnR ? gm0[r]
+                        : gamma    ? gm4[q]
+                                   : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        const float4 h = hl[q];
+        const float4 v = make_float4((h.x * c) * gm.x, (h.y * c) * gm.y, (h.z * c) * gm.z,
+                                     (h.w * c) * gm.w);
+        hl[q] = v;
+        amax = fmaxf(fmaxf(amax, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
     }
     amax = wave_max_f32(amax);
-    if (lane == 0) red_f[wv] = amax;
+    if (lane == 0) sh.redf[wv] = amax;
     __syncthreads();
-    float a = red_f[0];
-#pragma unroll
-    for (int i = 1; i < kFfnThreads / 64; ++i) a = fmaxf(a, red_f[i]);
+    float a = sh.redf[0];
+    for (int w = 1; w < kFfnWaves; ++w) a = fmaxf(a, sh.redf[w]);
     const float s = quant_scale(a);
-    // Pass 3: codes of the thread's runs, 32 bytes per run in two stores.
+
+    // ---- pass 3: codes, four per 4-byte store
     int sum = 0;
-    int8_t *q = xq + row;
-    for (int r = tid; r < nruns; r += kFfnThreads) {
-        int w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t packed4 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = quant_one(hl[(i * 4 + e) * nruns + r], s);
-                sum += v;
-                packed4 |= (uint32_t)(uint8_t)(int8_t)v << (8 * e);
-            }
-            w[i] = (int)packed4;
-        }
-        int4 *dst = reinterpret_cast<int4 *>(q + r * 32);
-        dst[0] = make_int4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_int4(w[4], w[5], w[6], w[7]);
+    uint32_t *q4 = reinterpret_cast<uint32_t *>(xq + row);
+    for (int q = tid; q < nq; q += kFfnThreads) {
+        const float4 v = hl[q];
+        const int c0 = quant_one(v.x, s), c1 = quant_one(v.y, s), c2 = quant_one(v.z, s),
+                  c3 = quant_one(v.w, s);
+        sum += c0 + c1 + c2 + c3;
+        q4[q] = (uint32_t)(uint8_t)c0 | (uint32_t)(uint8_t)c1 << 8 |
+                (uint32_t)(uint8_t)c2 << 16 | (uint32_t)(uint8_t)c3 << 24;
     }
     sum = wave_sum_i32(sum);
-    if (lane == 0) red_i[wv] = sum;
+    if (lane == 0) sh.redi[wv] = sum;
     __syncthreads();
     if (tid == 0) {
         int t = 0;
-#pragma unroll
-        for (int i = 0; i < kFfnThreads / 64; ++i) t += red_i[i];
+        for (int w = 0; w < kFfnWaves; ++w) t += sh.redi[w];
         xs[blockIdx.x] = s;
         xsum[blockIdx.x] = t;
     }
@@ -146,7 +237,7 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
 hipError_t launch_ffn_act_quant(const float *g, const float *u, const float *gamma, float eps,
                                 int64_t N, int64_t F, int8_t *xq, float *xs, int32_t *xsum,
                                 hipStream_t st) {
-    const size_t lds = (size_t)F * sizeof(float) + (size_t)(F / 32) * sizeof(double);
+    const size_t lds = (size_t)F * sizeof(float);
     hipLaunchKernelGGL(ffn_act_quant_kernel, dim3((unsigned)N), dim3(kFfnThreads), lds, st, g, u,
                        gamma, eps, (int)F, xq, xs, xsum);
     return hipGetLastError();

@@ -15,7 +15,8 @@ Workloads (shapes as M x K = output rows x reduction length):
   KV heads of dim 128): q/o 2560x2560, k/v 640x2560, gate/up 6912x2560,
   down 2560x6912; uniform ternary; bf16 tokens.
 * ``b2_sparse`` -- the same shapes with p(0)=1/2, p(+1)=p(-1)=1/4 and bf16
-  tokens where odd token rows carry one +-20 outlier (20 sigma).
+  tokens where odd token rows carry one +-20 outlier (20 sigma); a single
+  token is run both plain and with one (``outliers="all"``).
 * ``e06``     -- 0.6B-class embedding model (hidden 1024, FFN 3072, 16 query
   heads of dim 128, 8 KV heads): q 2048x1024, k/v 1024x1024, o 1024x2048,
   gate/up 3072x1024, down 1024x3072; uniform ternary; bf16 tokens.
@@ -100,15 +101,18 @@ def tokens_f32(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
 
 
 def tokens_bf16(rng: np.random.Generator, N: int, K: int,
-                outliers: bool = False,
+                outliers: bool | str = False,
                 orng: np.random.Generator | None = None) -> np.ndarray:
-    """bf16 bits [N][K]: N(0,1) samples rounded to bf16.  With ``outliers``,
-    every odd token row gets one element (seeded position and sign) set to
-    +-20.0, which is exact in bf16."""
+    """bf16 bits [N][K]: N(0,1) samples rounded to bf16.  With ``outliers``
+    (True or "odd"), every odd token row gets one element (seeded position and
+    sign) set to +-20.0, which is exact in bf16; with "all", every row does
+    (so a single token carries one too)."""
     x = tokens_f32(rng, N, K)
     if outliers:
+        if outliers not in (True, "odd", "all"):
+            raise ValueError(outliers)
         orng = orng or rng
-        for n in range(1, N, 2):
+        for n in range(0 if outliers == "all" else 1, N, 1 if outliers == "all" else 2):
             k = int(orng.integers(0, K))
             x[n, k] = np.float32(20.0 if orng.integers(0, 2) else -20.0)
     return f32_to_bf16_bits(x)

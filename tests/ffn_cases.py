@@ -60,3 +60,39 @@ def order_sensitive_token(F: int = 128):
     u[0, :len(h)] = np.array(h, np.float32)
     g = np.ones((1, F), np.float32)
     return g, u, eps, _factor(s_exact, F, eps), _factor(s_below, F, eps)
+
+
+def _powers_as_squares(j0: int, j1: int) -> list:
+    """h values whose squares are 2^-j for j0 <= j < j1: 2^-(j/2) for even j,
+    two copies of 2^-((j+1)/2) for odd j."""
+    h = []
+    for j in range(j0, j1):
+        if j % 2 == 0:
+            h.append(2.0 ** (-j // 2))
+        else:
+            h += [2.0 ** (-(j + 1) // 2)] * 2
+    return h
+
+
+def _token(h: list):
+    F = (len(h) + 127) // 128 * 128
+    u = np.zeros((1, F), np.float32)
+    u[0, :len(h)] = np.array(h, np.float32)
+    return np.ones((1, F), np.float32), u
+
+
+def carry_token(extra: int = 0):
+    """(g, u) of a token with squares 1, 2^-54 .. 2^-112 (every bit once) and
+    256 + extra squares of 2^-120.  The sum is 1 + 2^-53 - 2^-112 + (256 +
+    extra) * 2^-120: at extra = 0 exactly the midpoint 1 + 2^-53 (ties to
+    even: 1), above it for extra > 0 (1 + 2^-52), below for extra < 0 (1).
+    A sum that keeps 112 bits below 1 sees a run of ones down to the round
+    bit and only a count of the 2^-120 squares below it."""
+    return _token([1.0] + _powers_as_squares(54, 113) + [2.0 ** -60] * (256 + extra))
+
+
+def deep_carry_token():
+    """Squares 1, then every power 2^-54 .. 2^-224, then four of 2^-226: the
+    run of ones spans two 112-bit windows and the last four squares complete
+    the carry to exactly 1 + 2^-53 (a tie: rounds to 1)."""
+    return _token([1.0] + _powers_as_squares(54, 225) + [2.0 ** -113] * 4)

@@ -285,3 +285,49 @@ def test_binding_limits_match_header():
                         ("BITNET_LINEAR_FUSED_MAX_N", _binding.LINEAR_FUSED_MAX_N)):
         m = re.search(r"#define %s (\d+)" % name, text)
         assert m and int(m.group(1)) == value, name
+
+
+# ------------------------------------------- binding argument checks (no GPU)
+def _binding_cases():
+    import torch
+    import ternary_weight_i2_amd as bn
+    i8, u8, f32, i32 = torch.int8, torch.uint8, torch.float32, torch.int32
+    N, K, M = 3, 256, 40
+    xq = torch.zeros((N, K), dtype=i8)
+    xs = torch.zeros((N,), dtype=f32)
+    xsum = torch.zeros((N,), dtype=i32)
+    P = torch.zeros((M, K // 4), dtype=u8)
+    g = torch.zeros((N, 512), dtype=f32)
+    x = torch.zeros((N, K), dtype=f32)
+    return bn, [
+        # K of the weights does not match the tokens
+        lambda: bn.gemv(torch.zeros((M, K // 4 + 32), dtype=u8), 1.0, xq, xs, xsum),
+        lambda: bn.gemm(torch.zeros((M, K // 4), dtype=i8), 1.0, xq, xs, xsum),
+        lambda: bn.gemv_lut(P, 1.0, xq.to(f32), xs, xsum),
+        lambda: bn.gemv(P, 1.0, xq, xs[:2], xsum),
+        lambda: bn.gemv(P, 1.0, xq, xs, xsum.to(torch.int64)),
+        # short or mistyped caller outputs
+        lambda: bn.gemv(P, 1.0, xq, xs, xsum, out=(torch.zeros((N, M - 1), dtype=i32), None)),
+        lambda: bn.gemm(P, 1.0, xq, xs, xsum, out=(None, torch.zeros((N, M), dtype=torch.float64))),
+        lambda: bn.quant_act(x, out=(xq[:, :128], xs, xsum)),
+        lambda: bn.ffn_act_quant(g, g, gamma=torch.zeros(256, dtype=f32)),
+        lambda: bn.ffn_act_quant(g, g, out=(torch.zeros((N, 256), dtype=i8), xs, xsum)),
+        lambda: bn.gemm_group([(P, 1.0), (torch.zeros((7, K // 8), dtype=u8), 1.0)], xq, xs, xsum),
+        lambda: bn.gemv_group([(P, 1.0)], xq, xs, xsum, out=[(None, torch.zeros((N + 1, M), dtype=f32))]),
+        lambda: bn.gemv_group([(P, 1.0)] * 9, xq, xs, xsum),
+        lambda: bn.linear(x, [(torch.zeros((M, K // 2), dtype=u8), 1.0)]),
+        lambda: bn.linear(x, [(P, 1.0)], qout=(xq, xs, xsum[:1])),
+        lambda: bn.absmean_pack(x, out=torch.zeros((N, K // 8), dtype=u8)),
+        lambda: bn.pack(torch.zeros((2, 130), dtype=i8)),
+    ]
+
+
+def test_binding_refuses_bad_tensors_before_any_launch():
+    """Every malformed tensor (wrong K, dtype or length, short output buffer)
+    raises in the binding on the host -- these are CPU tensors, so reaching
+    data_ptr() or the library would raise a different error."""
+    bn, cases = _binding_cases()
+    for i, case in enumerate(cases):
+        with pytest.raises((TypeError, ValueError)) as e:
+            case()
+        assert "must live on the GPU" not in str(e.value), (i, str(e.value))

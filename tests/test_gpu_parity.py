@@ -67,6 +67,8 @@ def run_case(bn, M, K, N, entry, dist="uniform", seed=0, act="bf16", outliers=Fa
     else:
         x = synth.tokens_bf16(rng, N, K, outliers=outliers)
         x_gpu = to_bf16_tensor(x)
+        if outliers == "all":
+            assert (np.abs(synth.bf16_bits_to_f32(x)).max(axis=1) == 20.0).all()
     # GPU path
     P_gpu = bn.pack(dev(W))
     xq, xs, xsum = bn.quant_act(x_gpu)
@@ -297,19 +299,37 @@ def test_large_layer_sampled(bn, proj, N):
     run_case(bn, M, K, N, "gemv", seed=N + 100 * len(proj), rows=rows)
 
 
+@pytest.mark.parametrize("outliers", [False, "all"])
+@pytest.mark.parametrize("entry", ["gemv", "lut", "linear"])
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_b2_sparse_single_token(bn, proj, entry, outliers):
+    """The sparse 2B-class workload at N = 1, plain and with one +-20
+    outlier in the token: the int8 GEMV, the lookup-table GEMV and the fused
+    bf16 linear, every row against the oracle."""
+    M, K = synth.SHAPES["b2_sparse"][proj]
+    seed = 7000 + 10 * synth.PROJ_NAMES.index(proj) + (1 if outliers else 0)
+    if entry == "linear":
+        run_linear(bn, [M], K, 1, "bf16", seed=seed, outliers=outliers, dist="half_zero")
+    else:
+        run_case(bn, M, K, 1, entry, dist="half_zero", outliers=outliers, seed=seed)
+
+
 # ------------------------------------------------------ fused decode linear
 def make_x(rng, N, K, dtype, outliers=False):
     if dtype == "f32":
         x = synth.tokens_f32(rng, N, K)
         return x, dev(x)
     x = synth.tokens_bf16(rng, N, K, outliers=outliers)
+    if outliers == "all":
+        assert (np.abs(synth.bf16_bits_to_f32(x)).max(axis=1) == 20.0).all()
     return x, to_bf16_tensor(x)
 
 
-def run_linear(bn, Ms, K, N, dtype, seed, rows=None, outliers=False, check_unfused=True):
+def run_linear(bn, Ms, K, N, dtype, seed, rows=None, outliers=False, check_unfused=True,
+               dist="uniform"):
     """Fused quantise + grouped GEMV vs the oracle and vs the unfused calls."""
     rng = np.random.default_rng(seed)
-    Ws = [synth.ternary(rng, M, K) for M in Ms]
+    Ws = [synth.ternary(rng, M, K, dist) for M in Ms]
     alphas = [synth.weight_scale(rng) for _ in Ms]
     x, xg = make_x(rng, N, K, dtype, outliers)
     Ps = [bn.pack(dev(W)) for W in Ws]
@@ -456,11 +476,9 @@ def test_linear_e06_prefill_layer(bn):
 
 # ------------------------------------------------ one-time weight conversion
 def check_absmean(bn, W, bits=None):
-    """AbsMean ternariser on the GPU vs the oracle.  alpha: the same fp32 value
-    (the binary64 sums may differ in their last bits only, so 1 ulp is allowed);
-    codes: bit for bit with the oracle's ternary step taken at the GPU's alpha
-    (the decision in the same precision), and with the oracle's own result
-    whenever the two alphas agree."""
+    """AbsMean ternariser on the GPU vs the oracle, bit for bit: alpha (both
+    sides take the exactly rounded sum of |w|, so no summation order enters)
+    and the packed codes."""
     if bits is not None:
         wg = to_bf16_tensor(bits)
         host = bits
@@ -469,14 +487,9 @@ def check_absmean(bn, W, bits=None):
         host = W
     packed, alpha = bn.absmean_pack(wg)
     torch.cuda.synchronize()
-    a_ref = oracle.absmean_alpha(host)
-    assert abs(np.float32(alpha) - np.float32(a_ref)) <= np.spacing(np.float32(a_ref))
-    q_at_gpu_alpha = oracle.absmean_ternary(host, alpha)
-    P_ref, bad = oracle.pack_i2s(q_at_gpu_alpha)
-    assert bad == 0
+    P_ref, a_ref, _ = oracle.absmean_i2s(host)
+    assert np.float32(alpha).view(np.uint32) == np.float32(a_ref).view(np.uint32)
     np.testing.assert_array_equal(packed.cpu().numpy(), P_ref)
-    if np.float32(alpha) == np.float32(a_ref):
-        np.testing.assert_array_equal(packed.cpu().numpy(), oracle.absmean_i2s(host)[0])
     return packed, alpha
 
 
@@ -506,6 +519,24 @@ def test_absmean_page_example_and_edges(bn):
     T = synth.ternary(rng, 33, 512)
     packed, alpha = check_absmean(bn, T.astype(np.float32) * np.float32(0.125))
     np.testing.assert_array_equal(packed.cpu().numpy(), oracle.pack_i2s(T)[0])
+
+
+def test_absmean_sum_is_exact(bn):
+    """Weights whose fixed-order binary64 sums of |w| straddle an fp32
+    rounding point: [4, 2^-22, 2^-51, 2^-51] (then zeros) has the exact mean
+    (1 + 2^-24 + 2^-52) / 32, above the fp32 midpoint, so alpha = (1 + 2^-23) / 32
+    whichever order the sum takes; spread over rows and workgroups too."""
+    W = np.zeros((1, 128), np.float32)
+    W[0, :4] = [4.0, 2.0 ** -22, 2.0 ** -51, 2.0 ** -51]
+    _, alpha = check_absmean(bn, W)
+    assert np.float32(alpha) == np.float32(1 + 2.0 ** -23) / np.float32(32)
+    big = np.zeros((2048, 1024), np.float32)
+    big.reshape(-1)[[0, 700001, 1500007, 2097151]] = [4.0, 2.0 ** -22, 2.0 ** -51, 2.0 ** -51]
+    big.reshape(-1)[5] = 1.0
+    check_absmean(bn, big)
+    rng = np.random.default_rng(12)
+    wide = (rng.standard_normal((64, 1024)) * np.exp2(rng.integers(-140, 100, (64, 1024)))).astype(np.float32)
+    check_absmean(bn, wide)
 
 
 def test_absmean_rejects_non_finite(bn):
@@ -638,6 +669,26 @@ def test_ffn_act_quant(bn, N, F, eps, with_gamma):
     u = (rng.standard_normal((N, F)) * 0.5).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, F).astype(np.float32) if with_gamma else None
     check_ffn_act(bn, g, u, gamma, eps)
+
+
+def test_ffn_factor_takes_the_exact_sum(bn):
+    """A token whose left-to-right binary64 sum of squares drops one ulp that
+    the exact sum keeps, where that ulp changes the fp32 factor
+    (tests/ffn_cases.py): codes and scale bit for bit with the oracle, and
+    the big channel's code follows the exact factor."""
+    import ffn_cases
+    g, u, eps, c_exact, c_ltr = ffn_cases.order_sensitive_token()
+    check_ffn_act(bn, g, u, None, eps)
+
+
+@pytest.mark.parametrize("extra", [-1, 0, 1, 5])
+def test_ffn_sum_carry_cases(bn, extra):
+    """Squares whose window sums leave a run of ones down to the round bit, so
+    the count of sub-window squares decides a carry: the kernel must add the
+    next windows (ties to even at extra = 0, up above, down below)."""
+    import ffn_cases
+    for g, u in (ffn_cases.carry_token(extra), ffn_cases.deep_carry_token()):
+        check_ffn_act(bn, g, u, None, float(np.float32(1.4e-45)))
 
 
 def test_ffn_act_quant_edges(bn):

@@ -829,3 +829,22 @@ def test_ffn_factor_takes_the_exact_sum(orc):
     q, s, qs, v = orc.ffn_act_quant(g, u, None, eps)
     assert v[0, 0] == np.float32(11.0) * c_exact
     assert v[0, 0] != np.float32(11.0) * c_ltr
+
+
+def test_ffn_carry_tokens_follow_the_exact_sum(orc):
+    """Constructed tokens (tests/ffn_cases.py) whose sum of squares is the
+    midpoint 1 + 2^-53 or just beside it: the oracle's factor is the one of
+    math.fsum's sum (ties to even), checked through v = h * c."""
+    import math
+    import ffn_cases
+    eps = float(np.float32(1.4e-45))
+    cases = [ffn_cases.carry_token(e) for e in (-1, 0, 1)] + [ffn_cases.deep_carry_token()]
+    sums = []
+    for g, u in cases:
+        F = u.shape[1]
+        S = math.fsum(u[0].astype(np.float64) ** 2)
+        sums.append(S)
+        c = np.float32(1.0 / math.sqrt(S / F + eps))
+        _, _, _, v = orc.ffn_act_quant(g, u, None, eps)
+        np.testing.assert_array_equal(v[0].view(np.uint32), (u[0] * c).view(np.uint32))
+    assert sums == [1.0, 1.0, 1.0 + 2.0 ** -52, 1.0]
