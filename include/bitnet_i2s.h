@@ -199,10 +199,11 @@ int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
  *   xq, x_scale, x_sum   outputs as bitnet_quant_act_i8 writes them, ready
  *            for bitnet_gemv_i2s_i8 / bitnet_gemm_i2s_i8 with the down weights.
  *
- * Per token: h = (relu(g)^2) * u in fp32; ss = sum of h^2 in binary64 over
- * runs of 32 channels in index order, then the run sums in index order;
- * c = fp32(1 / sqrt(ss / F + eps)); v = (h * c) * gamma in fp32; then per-token
- * absmax int8 quantisation of v.  0 <= N < 2^31; N == 0 is a no-op.
+ * Per token: h = (relu(g)^2) * u in fp32; ss = the sum of the F squares h^2
+ * (each exact in binary64) computed exactly and rounded once to binary64,
+ * to nearest-even -- no summation order enters; c = fp32(1 / sqrt(ss / F +
+ * eps)); v = (h * c) * gamma in fp32; then per-token absmax int8 quantisation
+ * of v.  0 <= N < 2^31; N == 0 is a no-op.
  */
 int bitnet_ffn_act_quant_i8(const float *g, const float *u, const float *gamma, float eps,
                             int64_t N, int64_t F, int8_t *xq, float *x_scale,
@@ -252,14 +253,16 @@ int bitnet_gemm_i2s_i8_group(const bitnet_i2s_matrix *mats, int n_mats, int64_t 
  *           16-byte aligned; M >= 1.
  *   packed  device [M][K/4] I2_S output, 16-byte aligned.
  *   alpha   HOST pointer; receives the per-tensor scale
- *           alpha = max(mean |w| over all M*K weights, 1e-5), the sum of |w|
- *           taken in binary64 in a fixed order and the mean rounded once to
- *           fp32.  Use it as w_scale of the matmul calls.
+ *           alpha = max(mean |w| over all M*K weights, 1e-5): the sum of |w|
+ *           computed exactly and rounded once to binary64 (so it depends on
+ *           no summation order), divided by M*K in binary64, rounded to fp32.
+ *           Use it as w_scale of the matmul calls.
  *
  * Each weight becomes q = clip(round-half-even(w / alpha), -1, 1), w / alpha
  * one fp32 division, stored as code q + 1.  Synchronises `stream`
  * (the scale is returned on the host); calls are serialised inside the
- * library.  Non-finite weights -> BITNET_E_VALUE (packed then unspecified).
+ * library.  Non-finite weights -> BITNET_E_VALUE (packed then unspecified);
+ * M * K above 2^40 -> BITNET_E_SHAPE.
  */
 int bitnet_absmean_i2s(const void *w, int dtype, int64_t M, int64_t K,
                        uint8_t *packed, float *alpha, void *stream);
