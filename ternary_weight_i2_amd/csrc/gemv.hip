@@ -35,11 +35,24 @@ struct GemvGeometry {
     int lpr;           // lanes per row
     int rows_per_wg;   // rows per workgroup
     int per;           // tokens per pass
+    bool long_rows;    // 16-wave workgroups, one row group per wave
 };
+// Long rows (a whole wave per row and more than four chunks per lane, i.e.
+// K > 16384) in a launch of at least 4096 rows take 16-wave workgroups of 16
+// rows: each wave then owns exactly one row and issues all its loads at once
+// (with 4 waves and 1024 workgroups each wave walked two rows, one memory
+// round trip after the other), and a token is staged once per 16 rows
+// instead of per 8.
 static GemvGeometry gemv_geometry(int64_t K, int64_t total_rows, int mode) {
     GemvGeometry g;
     const int C = (int)(K >> 6);
     g.lpr = BITNET_GEMV_LPR ? BITNET_GEMV_LPR : pick_lpr(C, total_rows);
+    g.long_rows = g.lpr == 64 && C > 4 * 64 && total_rows >= 4096;
+    if (g.long_rows) {
+        g.rows_per_wg = kGemvWavesLong;
+        g.per = (int)(kLdsBytes / K) < 2 ? 1 : 2;
+        return g;
+    }
     const int rows_per_iter = kGemvWaves * (64 / g.lpr);   // rows per workgroup row-group step
     // Row groups per workgroup: one (every load in flight at once, a single
     // scheduling round) unless that would need more than ~1024 workgroups.
@@ -92,12 +105,15 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
         // J <= 4: short-row kernels with exactly 3 or 4 chunk slots
         const int jn = (C + lpr - 1) / lpr;
         const int sr = nt == 1 && jn <= 4 ? (jn <= 3 ? 3 : 4) : 0;
+        const bool lr = geo.long_rows;
         if (nt == 1)
-            e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, sr, g, st)
-              : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, sr, g, st) : launch_gemv_nt<1, 2>(a, lpr, sr, g, st);
+            e = mode == 0 ? launch_gemv_nt<1, 0>(a, lpr, sr, lr, g, st)
+              : mode == 1 ? launch_gemv_nt<1, 1>(a, lpr, sr, lr, g, st)
+                          : launch_gemv_nt<1, 2>(a, lpr, sr, lr, g, st);
         else
-            e = mode == 0 ? launch_gemv_nt<2, 0>(a, lpr, sr, g, st)
-              : mode == 1 ? launch_gemv_nt<2, 1>(a, lpr, sr, g, st) : launch_gemv_nt<2, 2>(a, lpr, sr, g, st);
+            e = mode == 0 ? launch_gemv_nt<2, 0>(a, lpr, sr, lr, g, st)
+              : mode == 1 ? launch_gemv_nt<2, 1>(a, lpr, sr, lr, g, st)
+                          : launch_gemv_nt<2, 2>(a, lpr, sr, lr, g, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -1,6 +1,7 @@
-// gemv_valu.h -- decode matmul (a few tokens) on the vector ALUs: the kernel
-// template, instantiated per token count in gemv_valu_n{1,2,4,8}.hip (so the
-// four compile in parallel) and launched from gemv.hip.
+// gemv_valu.h -- decode matmul (one or two tokens per pass) on the vector
+// ALUs: the kernel template, instantiated per token count in gemv_valu_n1.hip
+// and gemv_valu_n2.hip (so the two compile in parallel) and launched from
+// gemv.hip.
 //
 // Pages: [P2] "[분석/검증-3] BitNet.cpp ARM 커널 재작성" §3 and [P3] "[기술 분석
 // 보고서] ARM64 ... 1.58-bit ..." §3.1-§4 (raw codes 0/1/2 multiply the
@@ -9,8 +10,9 @@
 // weights), §4-3 (a weight block is loaded once and reused for several
 // activation columns), §4-5 (per-token activation scale).
 //
-// Work split (gfx950, wave64): a workgroup of 4 waves owns `rows_per_wg`
-// consecutive rows of one matrix, walked in row groups (see the kernel).  A
+// Work split (gfx950, wave64): a workgroup of 4 waves (16 for long rows, see
+// gemv.hip) owns `rows_per_wg` consecutive rows of one matrix, walked in row
+// groups (see the kernel).  A
 // row is read as 16-byte chunks (coalesced dwordx4 loads, each packed byte
 // fetched exactly once).  A 16-byte chunk c is
 // half an I2_S block (b = c/2, half h = c%2): dword j holds block bytes
@@ -43,8 +45,8 @@
 
 namespace bitnet {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kGemvWaves = 4;        // waves per workgroup (WAVES), short and mid rows
+constexpr int kGemvWavesLong = 16;   // waves per workgroup for long rows (one row group each)
 constexpr int kLdsBytes = 61440;   // activation staging budget per workgroup (60 KiB)
 #ifndef BITNET_GEMV_TARGET_WGS
 #define BITNET_GEMV_TARGET_WGS 1024   // workgroups per launch before slabs grow
@@ -96,15 +98,16 @@ __device__ __forceinline__ int lds_pos(int t, int K, int k) {
 // from clamped, always-valid addresses (a repeated last piece cannot change
 // the absmax and is not emitted); finish() then reduces and quantises.
 // Longer tokens are streamed through twice (absmax pass, quantise pass).
-template <int NT, int MODE>
+template <int NT, int MODE, int WAVES>
 struct TokenPrologue {
+    static constexpr int kThreads = WAVES * 64;
     using V = TokVec<MODE>;
     static constexpr int E = V::kElems;
     static constexpr int XR = NT == 1 ? 4 : (NT == 2 ? 2 : 1);   // register budget
     uint4 raw[NT][XR];      // token bits as loaded; widened only in finish()
 
     __device__ static bool fits(const GemvArgs &a) {
-        return NT <= 2 && a.K / E <= XR * kGemvThreads;
+        return NT <= 2 && a.K / E <= XR * kThreads;
     }
     __device__ void load_tokens(const GemvArgs &a) {
         const int nq = a.K / E;
@@ -116,7 +119,7 @@ struct TokenPrologue {
 #pragma unroll
             for (int r = 0; r < XR; ++r)
                 raw[t][r] = reinterpret_cast<const uint4 *>(x + tt * rowb)[min(
-                    (int)threadIdx.x + r * kGemvThreads, nq - 1)];
+                    (int)threadIdx.x + r * kThreads, nq - 1)];
         }
     }
     __device__ void finish(const GemvArgs &a, bool in_regs, int8_t *xl, float *s_tok,
@@ -139,7 +142,7 @@ struct TokenPrologue {
                         for (int e = 0; e < E; ++e) am[t] = fmaxf(am[t], fabsf(v[e]));
                     }
                 } else {
-                    for (int q = tid; q < nq; q += kGemvThreads) {
+                    for (int q = tid; q < nq; q += kThreads) {
                         float v[E];
                         V::load(x + t * rowb, q, v);
 #pragma unroll
@@ -160,7 +163,7 @@ struct TokenPrologue {
         for (int t = 0; t < NT; ++t) {
             float amx = redf[0][t];
 #pragma unroll
-            for (int w = 1; w < kGemvWaves; ++w) amx = fmaxf(amx, redf[w][t]);
+            for (int w = 1; w < WAVES; ++w) amx = fmaxf(amx, redf[w][t]);
             s[t] = quant_scale(amx);
             sm[t] = 0;
         }
@@ -191,13 +194,13 @@ struct TokenPrologue {
                 if (in_regs) {
 #pragma unroll
                     for (int r = 0; r < XR; ++r) {
-                        const int q = tid + r * kGemvThreads;
+                        const int q = tid + r * kThreads;
                         float v[E];
                         V::widen(raw[t][r], v);
                         if (q < nq) emit(t, q, v);
                     }
                 } else {
-                    for (int q = tid; q < nq; q += kGemvThreads) {
+                    for (int q = tid; q < nq; q += kThreads) {
                         float v[E];
                         V::load(x + t * rowb, q, v);
                         emit(t, q, v);
@@ -214,7 +217,7 @@ struct TokenPrologue {
         if (tid < NT && tid < a.ntok) {
             int total = 0;
 #pragma unroll
-            for (int w = 0; w < kGemvWaves; ++w) total += redi[w][tid];
+            for (int w = 0; w < WAVES; ++w) total += redi[w][tid];
             s_tok[tid] = s[tid];
             sum_tok[tid] = total;
             if (blockIdx.x == 0) {
@@ -237,16 +240,17 @@ struct TokenPrologue {
 // chunk loop has no run-time guard (chunks past J carry zeroed weights), so
 // the compiler can issue every chunk's LDS reads at once -- the tail after the
 // weights arrive is a latency chain in these small launches.
-template <int NT, int LPR, int MODE, int JM>
-__global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs a) {
+template <int NT, int LPR, int MODE, int JM, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a) {
+    constexpr int kThreads = WAVES * 64;
     constexpr bool kAllChunks = JM <= 4;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
     int8_t *xl = reinterpret_cast<int8_t *>(lds);
     __shared__ float s_tok[NT];
     __shared__ int sum_tok[NT];
-    __shared__ float redf[kGemvWaves][NT];
-    __shared__ int redi[kGemvWaves][NT];
+    __shared__ float redf[WAVES][NT];
+    __shared__ int redi[WAVES][NT];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int sub = lane / LPR, u = lane % LPR;
@@ -262,9 +266,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
     const int wg_local = (int)blockIdx.x - a.mat[mi].wg_begin;
     const int row0 = wg_local * a.rows_per_wg;
     const int row1 = min(M, row0 + a.rows_per_wg);
-    // row groups of this wave: rows row0 + (g*4 + wv)*RG + sub
-    const int ngroups = (row1 - row0 + RG * kGemvWaves - 1) / (RG * kGemvWaves);
-    auto group_row = [&](int g) { return row0 + (g * kGemvWaves + wv) * RG + sub; };
+    // row groups of this wave: rows row0 + (g*WAVES + wv)*RG + sub
+    const int ngroups = (row1 - row0 + RG * WAVES - 1) / (RG * WAVES);
+    auto group_row = [&](int g) { return row0 + (g * WAVES + wv) * RG + sub; };
     // Every lane issues exactly JM loads per row group, from a clamped (always
     // valid) address; lanes or rows outside the matrix are zeroed after the
     // load.  A fixed, branch-free load count lets the compiler wait for just
@@ -286,8 +290,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
     if constexpr (MODE == 0) {
         const int n16 = a.ntok * (K >> 4);
         const int4 *src = reinterpret_cast<const int4 *>(a.x);
-        if (n16 <= 2 * kGemvThreads) {           // two int4 pieces per thread in registers
-            const int q0 = tid, q1 = tid + kGemvThreads;
+        if (n16 <= 2 * kThreads) {               // two int4 pieces per thread in registers
+            const int q0 = tid, q1 = tid + kThreads;
             const int4 p0 = src[min(q0, n16 - 1)];
             const int4 p1 = src[min(q1, n16 - 1)];
             __builtin_amdgcn_sched_barrier(0);   // keep the token loads ahead of the weights
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
             }
         } else {
             load_group(0, cur);
-            for (int q = tid; q < n16; q += kGemvThreads) {
+            for (int q = tid; q < n16; q += kThreads) {
                 const int t = q / (K >> 4), k = (q - t * (K >> 4)) << 4;
                 *reinterpret_cast<int4 *>(xl + lds_pos(t, K, k)) = src[q];
             }
@@ -314,8 +318,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
             sum_tok[tid] = a.xsum_in[tid];
         }
     } else {
-        TokenPrologue<NT, MODE> tp;
-        const bool in_regs = TokenPrologue<NT, MODE>::fits(a);
+        TokenPrologue<NT, MODE, WAVES> tp;
+        const bool in_regs = TokenPrologue<NT, MODE, WAVES>::fits(a);
         if (in_regs) tp.load_tokens(a);
         __builtin_amdgcn_sched_barrier(0);       // keep the token loads ahead of the weights
         load_group(0, cur);
@@ -387,27 +391,33 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_valu_kernel(const GemvArgs 
 }
 
 // One launch of the kernel for NT tokens per pass, token mode MODE and the
-// lane count chosen by the host.  Each (NT, MODE) pair is instantiated in one
-// of the gemv_valu_n*.hip translation units.
+// lane count chosen by the host.
 template <int NT, int MODE, int JM>
 static hipError_t launch_gemv_ntj(const GemvArgs &a, int lpr, unsigned grid, hipStream_t st) {
     const size_t lds = (size_t)a.ntok * (size_t)a.K;
+    const dim3 b(kGemvWaves * 64);
     switch (lpr) {
-        case 8: hipLaunchKernelGGL((gemv_valu_kernel<NT, 8, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((gemv_valu_kernel<NT, 16, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((gemv_valu_kernel<NT, 32, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
-        default: hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE, JM>), dim3(grid), dim3(kGemvThreads), lds, st, a); break;
+        case 8: hipLaunchKernelGGL((gemv_valu_kernel<NT, 8, MODE, JM, kGemvWaves>), dim3(grid), b, lds, st, a); break;
+        case 16: hipLaunchKernelGGL((gemv_valu_kernel<NT, 16, MODE, JM, kGemvWaves>), dim3(grid), b, lds, st, a); break;
+        case 32: hipLaunchKernelGGL((gemv_valu_kernel<NT, 32, MODE, JM, kGemvWaves>), dim3(grid), b, lds, st, a); break;
+        default: hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE, JM, kGemvWaves>), dim3(grid), b, lds, st, a); break;
     }
     return hipGetLastError();
 }
 
 // One launch of the kernel for NT tokens per pass, token mode MODE and the
-// lane count chosen by the host (short: J <= 4, taken for NT == 1 only).
-// Each (NT, MODE) pair is instantiated in one of the gemv_valu_n*.hip
-// translation units.
+// lane count chosen by the host (short: J <= 4, taken for NT == 1 only;
+// long: 16 waves of 64 lanes per row).  Each (NT, MODE) pair is
+// instantiated in one of the gemv_valu_n*.hip translation units.
 template <int NT, int MODE>
-hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, unsigned grid,
-                          hipStream_t st) {
+hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, bool long_rows,
+                          unsigned grid, hipStream_t st) {
+    if (long_rows) {
+        const size_t lds = (size_t)a.ntok * (size_t)a.K;
+        hipLaunchKernelGGL((gemv_valu_kernel<NT, 64, MODE, 8, kGemvWavesLong>), dim3(grid),
+                           dim3(kGemvWavesLong * 64), lds, st, a);
+        return hipGetLastError();
+    }
     if constexpr (NT == 1) {
         if (short_j == 3) return launch_gemv_ntj<NT, MODE, 3>(a, lpr, grid, st);
         if (short_j == 4) return launch_gemv_ntj<NT, MODE, 4>(a, lpr, grid, st);
@@ -416,7 +426,8 @@ hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, unsigned grid
 }
 
 #define BITNET_GEMV_EXTERN(NT, MODE) \
-    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, int, unsigned, hipStream_t)
+    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, int, bool, unsigned, \
+                                                        hipStream_t)
 // passes of one or two tokens (larger batches run on MFMA)
 BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);
 BITNET_GEMV_EXTERN(2, 0); BITNET_GEMV_EXTERN(2, 1); BITNET_GEMV_EXTERN(2, 2);

@@ -376,6 +376,17 @@ def test_linear_small(bn, Ms, K, N, dtype):
     run_linear(bn, Ms, K, N, dtype, seed=sum(Ms) + K + N)
 
 
+@pytest.mark.parametrize("Ms,K,N,dtype", [((4100,), 28672, 1, "bf16"), ((4100,), 28672, 2, "f32"),
+                                          ((2050, 2070), 32768, 2, "bf16"),
+                                          ((4097,), 16512, 1, "bf16"), ((4111,), 28672, 1, "f32")])
+def test_linear_long_rows(bn, Ms, K, N, dtype):
+    """Long rows (K > 16384, a whole wave per row) in launches of at least
+    4096 rows run 16-wave workgroups of 16 rows: M ragged against them, one
+    and two tokens per pass, fused linear and the int8 GEMV, every row
+    against the oracle."""
+    run_linear(bn, list(Ms), K, N, dtype, seed=K + N + sum(Ms))
+
+
 @pytest.mark.parametrize("group", ["attn", "o", "ffn", "down"])
 def test_linear_b2_decode_groups(bn, group):
     """The benchmark's launch configuration: one fused launch per dependency
