@@ -88,6 +88,88 @@ __host__ __device__ __forceinline__ U128 window_bits(uint64_t v, int P, int b, b
     return r;
 }
 
+// The same as window_bits, without branches (one straight sequence of selects
+// per square, so the lanes of a wave never diverge) and with the square's
+// parts formed from the fp32 value here: adds the window bits of h^2 to acc
+// and counts a square with bits below b in cnt.  Shift counts are kept in
+// 0..63 so every shift is defined; out-of-range cases are selected away.
+template <bool MASKED>
+__host__ __device__ __forceinline__ void window_add(float h, int b, U128 &acc, uint32_t &cnt) {
+    uint32_t bits;
+    __builtin_memcpy(&bits, &h, 4);
+    bits &= 0x7fffffffu;
+    const uint32_t E = bits >> 23;
+    const uint32_t m = (bits & 0x7fffffu) | (E ? 0x800000u : 0u);
+    const uint64_t v = (uint64_t)m * m;
+    const int d = (E ? 2 * (int)E - 2 : 0) - b;
+    // bits below b: v >> s, s = -d (all of v when s >= 64)
+    const int s = d < 0 ? -d : 0;
+    const uint64_t vr = s < 64 ? v >> (s & 63) : 0;
+    const uint64_t below = s == 0 ? 0 : (s < 64 ? v << ((64 - s) & 63) : v);
+    // the rest shifted up by l = d (<= 112 at level 1)
+    const int l = d > 0 ? d : 0;
+    uint64_t lo = l < 64 ? vr << (l & 63) : 0;
+    uint64_t hi = l == 0 ? 0 : (l < 64 ? vr >> ((64 - l) & 63) : (l < 128 ? vr << ((l - 64) & 63) : 0));
+    if (MASKED) {
+        hi &= (1ull << (kWin - 64)) - 1;
+        if (l >= kWin) lo = hi = 0;
+    }
+    const uint64_t nlo = acc.lo + lo;
+    acc.hi += hi + (nlo < lo ? 1u : 0u);
+    acc.lo = nlo;
+    cnt += below != 0 ? 1u : 0u;
+}
+
+// Level 1 on the FP64 units.  With b the window's bottom position, the
+// square x = h^2 (exact in binary64) is split into three parts that are
+// exact multiples of 2^(b+75), 2^(b+37) and 2^b, each below 2^38 of its unit
+// (x < 2^(b+113) at level 1): part k = floor(x_k / u_k) * u_k with x_k what
+// the higher parts left, formed as fl(fl(x_k + sigma) - sigma), sigma =
+// 2^52 * u_k (x_k rounded to a multiple of u_k, exact), minus u_k where that
+// rounded up; x_k minus the part is exact.  Every part, and every sum of at
+// most 2^15 of them, is an integer multiple of its unit below 2^53 units, so
+// the three per-bin double accumulators are exact in any order.  What is left
+// below 2^b marks the square in cnt.  bin_unit(k) gives the scales.
+struct Bins3 {
+    double s[3];
+};
+__host__ __device__ __forceinline__ double pos_scale(int pos) {   // 2^(pos - 298)
+    return __builtin_ldexp(1.0, pos - 298);
+}
+__host__ __device__ __forceinline__ void window_add_f64(float h, const double *unit,
+                                                       const double *sigma, Bins3 &acc,
+                                                       uint32_t &cnt) {
+    const double hd = (double)h;
+    double x = hd * hd;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        double q = (x + sigma[k]) - sigma[k];
+        q = q > x ? q - unit[k] : q;
+        x = x - q;
+        acc.s[k] += q;
+    }
+    cnt += x != 0.0 ? 1u : 0u;
+}
+// The exact integer sum_k bins[k] / unit_k * 2^(shift_k), shift = 75, 37, 0,
+// unit_k = 2^(b + shift_k - 298) (each bins[k] an integer multiple of its
+// unit below 2^53 units).
+__host__ __device__ __forceinline__ U128 bins_to_u128(const double *bins, int b) {
+    U128 r{0, 0};
+    const int shift[3] = {75, 37, 0};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const double n = bins[k] * __builtin_ldexp(1.0, 298 - b - shift[k]);   // exact
+        const double nh = __builtin_floor(n * 0x1p-32);
+        const uint64_t v = ((uint64_t)(uint32_t)nh << 32) | (uint32_t)(n - nh * 0x1p32);
+        const int sh = shift[k];
+        const U128 t = sh == 0 ? U128{v, 0}
+                     : sh < 64 ? U128{v << sh, v >> (64 - sh)}
+                               : U128{0, v << (sh - 64)};
+        add128(r, t);
+    }
+    return r;
+}
+
 __host__ __device__ __forceinline__ int top_bit128(const U128 &a) {
     return a.hi ? 127 - __builtin_clzll(a.hi) : 63 - __builtin_clzll(a.lo);
 }

@@ -8,11 +8,13 @@
 // One workgroup per token, 512 threads on 16-byte pieces (four channels).
 // Pass 1 forms h = (relu(g)^2) * u in fp32, keeps it in LDS and finds max|h|.
 // The sub-norm's sum of squares is the exact sum rounded once to binary64
-// (exact_sum.h): every thread adds the bits of its squares that lie in a
-// 112-bit window below the largest square into a 128-bit integer and counts
-// the squares with bits below the window; the workgroup adds the integers and
-// counts, and one thread rounds -- or, when the count could carry into the
-// round bit, the workgroup adds further windows into an exact integer first.
+// (exact_sum.h): every thread splits the bits of its squares that lie in a
+// 112-bit window below the largest square into three exact binary64 bin sums
+// (straight-line FP64 code) and counts the squares with bits below the
+// window; the waves' totals meet in LDS and wave 0 forms the 128-bit window
+// integer and rounds -- or, when the count could carry into the round bit,
+// the workgroup adds further windows into an exact integer first.  Each
+// thread only ever touches its own pieces of h in LDS.
 // c = fp32(1 / sqrt(sum / F + eps)).  Pass 2: v = (h * c) * gamma in place
 // and its absmax; pass 3: the scale and the codes with the activation
 // quantiser's arithmetic.
@@ -26,25 +28,37 @@ constexpr int kFfnWaves = kFfnThreads / 64;
 constexpr int kFfnR = 4;   // 16-byte pieces per thread loaded together
 
 struct FfnShared {
-    uint64_t red[kFfnWaves][5];   // 32-bit digits of the window sums + count
-    float redf[kFfnWaves];
+    uint64_t red[kFfnWaves][5];   // per-wave window sums (32-bit digits) + count
+    double redb[kFfnWaves][3];    // per-wave level-1 bin sums (exact)
+    uint32_t redc[kFfnWaves];     // per-wave count of squares below the window
+    float redm[kFfnWaves];        // max|h| per wave
+    float redf[kFfnWaves];        // max|v| per wave
     int redi[kFfnWaves];
     uint32_t big[kBigDigits];
-    double ss;
-    float hmax;
-    float c;
-    int state;   // 0: sum decided, 1: more windows needed
+    float c;                      // the sub-norm factor
+    int more;                     // 1: another window level is needed
 };
 
+// 64-bit lane moves through DPP (two 32-bit moves), for the wave sums below.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
+    return (uint64_t)hi << 32 | lo;
+}
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += dpp_u64<kDppXor1>(v);
+    v += dpp_u64<kDppXor2>(v);
+    v += dpp_u64<kDppHalfMirror>(v);
+    v += dpp_u64<kDppMirror>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
     return v;
 }
 
-// Adds every thread's (a, cnt); thread 0 receives the totals.
-__device__ __forceinline__ void block_sum_window(const U128 &a, uint32_t cnt, FfnShared &sh,
-                                                 U128 *tot, uint64_t *tot_cnt) {
+// Every wave's sum of (a, cnt) into sh.red (as 32-bit digits, each total
+// below 2^42); the caller synchronises before reading them.
+__device__ __forceinline__ void wave_window_sums(const U128 &a, uint32_t cnt, FfnShared &sh) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     uint64_t d[5] = {a.lo & 0xffffffffu, a.lo >> 32, a.hi & 0xffffffffu, a.hi >> 32, cnt};
 #pragma unroll
@@ -53,42 +67,104 @@ __device__ __forceinline__ void block_sum_window(const U128 &a, uint32_t cnt, Ff
 #pragma unroll
         for (int i = 0; i < 5; ++i) sh.red[wv][i] = d[i];
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t D[5] = {0, 0, 0, 0, 0};
-        for (int w = 0; w < kFfnWaves; ++w)
+}
+// The workgroup totals from sh.red (the exact total is below 2^128).
+__device__ __forceinline__ void window_totals(const FfnShared &sh, U128 *tot, uint64_t *tot_cnt) {
+    uint64_t D[5] = {0, 0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 5; ++i) D[i] += sh.red[w][i];
-        // the digit sums are below 2^42; the exact total is below 2^128
-        U128 r{D[0], 0};
-        add128(r, U128{D[1] << 32, D[1] >> 32});
-        add128(r, U128{0, D[2]});
-        add128(r, U128{0, D[3] << 32});
-        *tot = r;
-        *tot_cnt = D[4];
-    }
+    for (int w = 0; w < kFfnWaves; ++w)
+#pragma unroll
+        for (int i = 0; i < 5; ++i) D[i] += sh.red[w][i];
+    U128 r{D[0], 0};
+    add128(r, U128{D[1] << 32, D[1] >> 32});
+    add128(r, U128{0, D[2]});
+    add128(r, U128{0, D[3] << 32});
+    *tot = r;
+    *tot_cnt = D[4];
 }
 
-// This thread's part of window level b: bits of its squares at positions
-// >= b (below b + kWin when masked), and how many squares have bits below b.
-__device__ __forceinline__ void window_pass(const float4 *hl, int nq, int b, bool masked,
-                                            U128 *acc, uint32_t *cnt) {
+__device__ __forceinline__ double wave_sum_f64(double v) {   // exact here: integer multiples below 2^53
+    uint64_t b;
+    __builtin_memcpy(&b, &v, 8);
+    auto add = [&](uint64_t o) {
+        double x, y;
+        __builtin_memcpy(&x, &b, 8);
+        __builtin_memcpy(&y, &o, 8);
+        x += y;
+        __builtin_memcpy(&b, &x, 8);
+    };
+    add(dpp_u64<kDppXor1>(b));
+    add(dpp_u64<kDppXor2>(b));
+    add(dpp_u64<kDppHalfMirror>(b));
+    add(dpp_u64<kDppMirror>(b));
+    add(__shfl_xor(b, 16, 64));
+    add(__shfl_xor(b, 32, 64));
+    double r;
+    __builtin_memcpy(&r, &b, 8);
+    return r;
+}
+
+// Level 1 of the window on the FP64 units (exact_sum.h, window_add_f64):
+// this thread's three bin sums and count.
+__device__ __forceinline__ void window_pass_f64(const float4 *hl, int nq, int b, Bins3 *acc,
+                                                uint32_t *cnt) {
+    const double unit[3] = {pos_scale(b + 75), pos_scale(b + 37), pos_scale(b)};
+    const double sigma[3] = {unit[0] * 0x1p52, unit[1] * 0x1p52, unit[2] * 0x1p52};
+    Bins3 a{{0.0, 0.0, 0.0}};
+    uint32_t c = 0;
+    int q = threadIdx.x;
+    for (; q + kFfnThreads < nq; q += 2 * kFfnThreads) {   // two pieces in flight
+        const float4 h0 = hl[q], h1 = hl[q + kFfnThreads];
+        window_add_f64(h0.x, unit, sigma, a, c);
+        window_add_f64(h0.y, unit, sigma, a, c);
+        window_add_f64(h0.z, unit, sigma, a, c);
+        window_add_f64(h0.w, unit, sigma, a, c);
+        window_add_f64(h1.x, unit, sigma, a, c);
+        window_add_f64(h1.y, unit, sigma, a, c);
+        window_add_f64(h1.z, unit, sigma, a, c);
+        window_add_f64(h1.w, unit, sigma, a, c);
+    }
+    if (q < nq) {
+        const float4 h0 = hl[q];
+        window_add_f64(h0.x, unit, sigma, a, c);
+        window_add_f64(h0.y, unit, sigma, a, c);
+        window_add_f64(h0.z, unit, sigma, a, c);
+        window_add_f64(h0.w, unit, sigma, a, c);
+    }
+    *acc = a;
+    *cnt = c;
+}
+
+__device__ __forceinline__ float norm_factor(double ss, int F, float eps) {
+    return (float)(1.0 / sqrt(ss / (double)F + (double)eps));
+}
+
+// This thread's part of window level b on the integer units: bits of its
+// squares at positions >= b (below b + kWin when MASKED), and how many
+// squares have bits below b (the rare further levels).
+template <bool MASKED>
+__device__ __forceinline__ void window_pass(const float4 *hl, int nq, int b, U128 *acc,
+                                            uint32_t *cnt) {
     U128 a{0, 0};
     uint32_t c = 0;
-    for (int q = threadIdx.x; q < nq; q += kFfnThreads) {
-        const float4 h4 = hl[q];
-        const float hv[4] = {h4.x, h4.y, h4.z, h4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint64_t v;
-            int P;
-            square_parts(hv[e], v, P);
-            if (v) {
-                bool rem;
-                add128(a, window_bits(v, P, b, masked, &rem));
-                c += rem ? 1u : 0u;
-            }
-        }
+    int q = threadIdx.x;
+    for (; q + kFfnThreads < nq; q += 2 * kFfnThreads) {   // two pieces in flight
+        const float4 h0 = hl[q], h1 = hl[q + kFfnThreads];
+        window_add<MASKED>(h0.x, b, a, c);
+        window_add<MASKED>(h0.y, b, a, c);
+        window_add<MASKED>(h0.z, b, a, c);
+        window_add<MASKED>(h0.w, b, a, c);
+        window_add<MASKED>(h1.x, b, a, c);
+        window_add<MASKED>(h1.y, b, a, c);
+        window_add<MASKED>(h1.z, b, a, c);
+        window_add<MASKED>(h1.w, b, a, c);
+    }
+    if (q < nq) {
+        const float4 h0 = hl[q];
+        window_add<MASKED>(h0.x, b, a, c);
+        window_add<MASKED>(h0.y, b, a, c);
+        window_add<MASKED>(h0.z, b, a, c);
+        window_add<MASKED>(h0.w, b, a, c);
     }
     *acc = a;
     *cnt = c;
@@ -137,19 +213,15 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
         }
     }
     hmax = wave_max_f32(hmax);
-    if (lane == 0) sh.redf[wv] = hmax;
+    if (lane == 0) sh.redm[wv] = hmax;
     __syncthreads();
-    if (tid == 0) {
-        float m = sh.redf[0];
-        for (int w = 1; w < kFfnWaves; ++w) m = fmaxf(m, sh.redf[w]);
-        sh.hmax = m;
-    }
-    __syncthreads();
+    float hm = sh.redm[0];
+#pragma unroll
+    for (int w = 1; w < kFfnWaves; ++w) hm = fmaxf(hm, sh.redm[w]);
 
-    // ---- the exactly rounded sum of h^2
-    const float hm = sh.hmax;
+    // ---- the exactly rounded sum of h^2 -> the factor c (wave 0 rounds)
     if (hm == 0.0f) {
-        if (tid == 0) sh.ss = 0.0;
+        if (tid == 0) sh.c = norm_factor(0.0, F, eps);
     } else {
         uint64_t vmax;
         int Pmax;
@@ -158,38 +230,64 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
         U128 acc, A;
         uint32_t cnt;
         uint64_t C;
-        window_pass(hl, nq, T - kWin, false, &acc, &cnt);
-        block_sum_window(acc, cnt, sh, &A, &C);
-        if (tid == 0) {
-            double s;
-            if (round_level1(A, C, T - kWin, &s)) {
-                sh.ss = s;
-                sh.state = 0;
-            } else {
-                for (int i = 0; i < kBigDigits; ++i) sh.big[i] = 0;
-                big_shift_add(sh.big, A);
-                sh.state = 1;
+        {
+            Bins3 bins;
+            window_pass_f64(hl, nq, T - kWin, &bins, &cnt);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) bins.s[k] = wave_sum_f64(bins.s[k]);
+            cnt = (uint32_t)wave_sum_i32((int)cnt);
+            if (lane == 0) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) sh.redb[wv][k] = bins.s[k];
+                sh.redc[wv] = cnt;
+            }
+        }
+        __syncthreads();
+        if (wv == 0) {
+            {
+                double tot[3] = {0.0, 0.0, 0.0};
+                C = 0;
+#pragma unroll
+                for (int w = 0; w < kFfnWaves; ++w) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) tot[k] += sh.redb[w][k];
+                    C += sh.redc[w];
+                }
+                A = bins_to_u128(tot, T - kWin);
+            }
+            double ss;
+            const bool done = round_level1(A, C, T - kWin, &ss);
+            if (lane == 0) {
+                sh.more = done ? 0 : 1;
+                if (done) {
+                    sh.c = norm_factor(ss, F, eps);
+                } else {
+                    for (int i = 0; i < kBigDigits; ++i) sh.big[i] = 0;
+                    big_shift_add(sh.big, A);
+                }
             }
         }
         __syncthreads();
         // Rare: a carry into the round bit is possible.  Add the next windows
-        // of every square until no square has bits left below the window
-        // (at most five levels cover the whole range of squares of fp32).
-        for (int k = 2; k <= 8 && sh.state == 1; ++k) {
+        // of every square into an exact integer until no square has bits left
+        // below the window (at most five levels cover the whole range of
+        // squares of fp32 values).
+        for (int k = 2; k <= 8 && sh.more; ++k) {
             const int b = T - kWin * k;
-            window_pass(hl, nq, b, true, &acc, &cnt);
-            block_sum_window(acc, cnt, sh, &A, &C);
+            window_pass<true>(hl, nq, b, &acc, &cnt);
+            wave_window_sums(acc, cnt, sh);
+            __syncthreads();
             if (tid == 0) {
+                window_totals(sh, &A, &C);
                 big_shift_add(sh.big, A);
                 if (C == 0) {
-                    sh.ss = big_round(sh.big, b);
-                    sh.state = 0;
+                    sh.c = norm_factor(big_round(sh.big, b), F, eps);
+                    sh.more = 0;
                 }
             }
             __syncthreads();
         }
     }
-    if (tid == 0) sh.c = (float)(1.0 / sqrt(sh.ss / (double)F + (double)eps));
     __syncthreads();
     const float c = sh.c;
 
