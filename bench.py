@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "8dae12b35d406b3067aacd15bf8c55f14c6ab51773f697c10b90425b2d8cfe9d",
-           "bytes_per_launch": 4574464}
+           "sha256": "afaad22f73bba8a5ec8524b96f2bd8f120989d74e28b40f7071eda13a32da31c",
+           "bytes_per_launch": 4578304}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))

@@ -38,16 +38,16 @@ struct GemvGeometry {
     bool long_rows;    // 16-wave workgroups, one row group per wave
 };
 // Long rows (a whole wave per row and more than four chunks per lane, i.e.
-// K > 16384) in a launch of at least 4096 rows take 16-wave workgroups of 16
-// rows: each wave then owns exactly one row and issues all its loads at once
-// (with 4 waves and 1024 workgroups each wave walked two rows, one memory
-// round trip after the other), and a token is staged once per 16 rows
-// instead of per 8.
+// K > 16384) quantised in the kernel (modes 1/2) in a launch of at least 4096
+// rows take 16-wave workgroups of 16 rows: the whole bf16 token then fits the
+// prologue's registers (read once per workgroup instead of twice), and each
+// wave owns one row.  On int8 tokens the 4-wave layout with two row groups
+// per wave is faster (down projection 8192x28672: 14.3 against 15.6 us).
 static GemvGeometry gemv_geometry(int64_t K, int64_t total_rows, int mode) {
     GemvGeometry g;
     const int C = (int)(K >> 6);
     g.lpr = BITNET_GEMV_LPR ? BITNET_GEMV_LPR : pick_lpr(C, total_rows);
-    g.long_rows = g.lpr == 64 && C > 4 * 64 && total_rows >= 4096;
+    g.long_rows = mode != 0 && g.lpr == 64 && C > 4 * 64 && total_rows >= 4096;
     if (g.long_rows) {
         g.rows_per_wg = kGemvWavesLong;
         g.per = (int)(kLdsBytes / K) < 2 ? 1 : 2;

@@ -290,13 +290,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a)
     if constexpr (MODE == 0) {
         const int n16 = a.ntok * (K >> 4);
         const int4 *src = reinterpret_cast<const int4 *>(a.x);
-        if (n16 <= 2 * kThreads) {               // two int4 pieces per thread in registers
-            const int q0 = tid, q1 = tid + kThreads;
-            const int4 p0 = src[min(q0, n16 - 1)];
-            const int4 p1 = src[min(q1, n16 - 1)];
-            __builtin_amdgcn_sched_barrier(0);   // keep the token loads ahead of the weights
-            load_group(0, cur);
-            __builtin_amdgcn_sched_barrier(0);
+        // The per-token scale and sum are loaded before the weights: loads
+        // complete in order, so storing a value loaded after them would wait
+        // for every weight load (and, through the barrier, stall every wave).
+        const int tsel = min(tid, a.ntok - 1);
+        const float xs_r = a.xs_in[tsel];
+        const int xsum_r = a.xsum_in[tsel];
+        // Short tokens: two 16-byte pieces per thread, loaded ahead of the
+        // weights and stored to LDS once the weight loads are issued.  Longer
+        // tokens are staged first.  Either way the weight loads of the first
+        // row group are issued by the same code after the branch, so the
+        // compiler's wait counts stay exact for every chunk below.
+        const bool in_regs = n16 <= 2 * kThreads;
+        const int q0 = tid, q1 = tid + kThreads;
+        int4 p0 = make_int4(0, 0, 0, 0), p1 = p0;
+        if (in_regs) {
+            p0 = src[min(q0, n16 - 1)];
+            p1 = src[min(q1, n16 - 1)];
+        } else {
+            for (int q = tid; q < n16; q += kThreads) {
+                const int t = q / (K >> 4), k = (q - t * (K >> 4)) << 4;
+                *reinterpret_cast<int4 *>(xl + lds_pos(t, K, k)) = src[q];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the token loads ahead of the weights
+        load_group(0, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        if (in_regs) {
             const int kp = K >> 4;
             if (q0 < n16) {
                 const int t = q0 / kp;
@@ -306,16 +326,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a)
                 const int t = q1 / kp;
                 *reinterpret_cast<int4 *>(xl + lds_pos(t, K, (q1 - t * kp) << 4)) = p1;
             }
-        } else {
-            load_group(0, cur);
-            for (int q = tid; q < n16; q += kThreads) {
-                const int t = q / (K >> 4), k = (q - t * (K >> 4)) << 4;
-                *reinterpret_cast<int4 *>(xl + lds_pos(t, K, k)) = src[q];
-            }
         }
         if (tid < NT && tid < a.ntok) {
-            s_tok[tid] = a.xs_in[tid];
-            sum_tok[tid] = a.xsum_in[tid];
+            s_tok[tid] = xs_r;
+            sum_tok[tid] = xsum_r;
         }
     } else {
         TokenPrologue<NT, MODE, WAVES> tp;
@@ -382,10 +396,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a)
             }
         }
     };
-    // Load a row group, then consume it (the first group's loads were issued
-    // before the activations were staged).
-    for (int g = 0; g < ngroups; ++g) {
-        if (g > 0) load_group(g, cur);
+    // Consume the first row group (its loads were issued before the
+    // activations were staged), then load and consume the others.  The first
+    // group stays outside the loop: with it inside, the compiler merged the
+    // loop entry (loads in flight) with the back edge (none) and waited for
+    // every load before the first dot product, so no chunk's arithmetic
+    // overlapped the later chunks' memory latency.
+    compute(0, cur);
+    for (int g = 1; g < ngroups; ++g) {
+        load_group(g, cur);
         compute(g, cur);
     }
 }

@@ -381,9 +381,9 @@ def test_linear_small(bn, Ms, K, N, dtype):
                                           ((4097,), 16512, 1, "bf16"), ((4111,), 28672, 1, "f32")])
 def test_linear_long_rows(bn, Ms, K, N, dtype):
     """Long rows (K > 16384, a whole wave per row) in launches of at least
-    4096 rows run 16-wave workgroups of 16 rows: M ragged against them, one
-    and two tokens per pass, fused linear and the int8 GEMV, every row
-    against the oracle."""
+    4096 rows: the fused linear runs 16-wave workgroups of 16 rows, the int8
+    GEMV 4-wave ones; M ragged against both, one and two tokens per pass,
+    every row against the oracle (and fused against unfused bit for bit)."""
     run_linear(bn, list(Ms), K, N, dtype, seed=K + N + sum(Ms))
 
 
