@@ -104,13 +104,19 @@ struct Vec16<0> {
         const float4 f = reinterpret_cast<const float4 *>(base)[i];
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
+    __device__ static void widen(const uint4 u, float *v) {
+        v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+        v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    }
 };
 
 template <>
 struct Vec16<1> {
     static constexpr int kElems = 8;
     __device__ static void load(const void *base, int64_t i, float *v) {
-        const uint4 u = reinterpret_cast<const uint4 *>(base)[i];
+        widen(reinterpret_cast<const uint4 *>(base)[i], v);
+    }
+    __device__ static void widen(const uint4 u, float *v) {
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -123,6 +129,8 @@ struct Vec16<1> {
 constexpr int kQuantThreads = 256;   // one workgroup per token
 constexpr int kQuantWaves = kQuantThreads / 64;
 
+// Rows longer than 16 pieces per thread (fp32 tokens above K = 16384): two
+// passes over the row (absmax, then quantise).
 template <int BF16>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const void *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
@@ -183,15 +191,98 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     }
 }
 
+// The same per-token quantisation with the row held in registers: every
+// thread issues the loads of all its R 16-byte pieces at once (clamped,
+// always-valid addresses; a repeated last piece cannot change the absmax and
+// is not emitted), so a token costs one memory round trip instead of one per
+// piece and pass.  Identical arithmetic, identical bits.
+template <int BF16, int R>
+__global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
+    const void *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
+    float *__restrict__ xs, int32_t *__restrict__ xsum) {
+    using V = Vec16<BF16>;
+    constexpr int E = V::kElems;
+    __shared__ float red_f[kQuantWaves];
+    __shared__ int red_i[kQuantWaves];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const char *row = reinterpret_cast<const char *>(x) + n * K * (BF16 ? 2 : 4);
+    const int nvec = (int)(K / E);
+
+    uint4 raw[R];   // the pieces as loaded; widened where used
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        raw[r] = reinterpret_cast<const uint4 *>(row)[min(tid + r * kQuantThreads, nvec - 1)];
+    float a = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float v[E];
+        V::widen(raw[r], v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(v[e]));
+    }
+    a = wave_max_f32(a);
+    if (lane == 0) red_f[wv] = a;
+    __syncthreads();
+    a = red_f[0];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) a = fmaxf(a, red_f[w]);
+    const float s = quant_scale(a);
+
+    int8_t *qrow = xq + n * K;
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + r * kQuantThreads;
+        if (i < nvec) {
+            float v[E];
+            V::widen(raw[r], v);
+            uint32_t packedq[E / 4];
+#pragma unroll
+            for (int j = 0; j < E / 4; ++j) packedq[j] = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int qi = quant_one(v[e], s);
+                sum += qi;
+                packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+            }
+            if (E == 8) {
+                reinterpret_cast<uint2 *>(qrow)[i] = make_uint2(packedq[0], packedq[E / 4 - 1]);
+            } else {
+                reinterpret_cast<uint32_t *>(qrow)[i] = packedq[0];
+            }
+        }
+    }
+    sum = wave_sum_i32(sum);
+    if (lane == 0) red_i[wv] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        xs[n] = s;
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < kQuantWaves; ++w) t += red_i[w];
+        xsum[n] = t;
+    }
+}
+
+template <int BF16>
+static hipError_t launch_quant_t(const void *x, int64_t N, int64_t K, int8_t *xq, float *xs,
+                                 int32_t *xsum, hipStream_t st) {
+    const int64_t per = (K / Vec16<BF16>::kElems + kQuantThreads - 1) / kQuantThreads;
+    const dim3 g((unsigned)N), b(kQuantThreads);
+    if (per <= 1) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1>), g, b, 0, st, x, K, xq, xs, xsum);
+    else if (per <= 2) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 2>), g, b, 0, st, x, K, xq, xs, xsum);
+    else if (per <= 4) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 4>), g, b, 0, st, x, K, xq, xs, xsum);
+    else if (per <= 8) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 8>), g, b, 0, st, x, K, xq, xs, xsum);
+    else if (per <= 16) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 16>), g, b, 0, st, x, K, xq, xs, xsum);
+    else hipLaunchKernelGGL(quant_act_kernel<BF16>, g, b, 0, st, x, K, xq, xs, xsum);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant(const void *x, int bf16, int64_t N, int64_t K,
                         int8_t *xq, float *xs, int32_t *xsum, hipStream_t st) {
-    if (bf16)
-        hipLaunchKernelGGL(quant_act_kernel<1>, dim3((unsigned)N), dim3(kQuantThreads), 0, st,
-                           x, K, xq, xs, xsum);
-    else
-        hipLaunchKernelGGL(quant_act_kernel<0>, dim3((unsigned)N), dim3(kQuantThreads), 0, st,
-                           x, K, xq, xs, xsum);
-    return hipGetLastError();
+    return bf16 ? launch_quant_t<1>(x, N, K, xq, xs, xsum, st)
+                : launch_quant_t<0>(x, N, K, xq, xs, xsum, st);
 }
 
 }  // namespace bitnet
