@@ -68,3 +68,15 @@ def test_defaults_are_one_gpu(monkeypatch, argv):
     monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
     a = bench.parse()
     assert a.gpus == 1 and a.steps >= 1 and a.warmup >= 0
+
+
+def test_recorded_mfma_busy_belongs_to_the_committed_gemm(tmp_path, monkeypatch):
+    assert bench.measured_mfma_busy() == bench.GEMM_COUNTERS["mfma_busy"]
+    for f in bench.GEMM_COUNTERS["sources"]:
+        dst = tmp_path / f
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, f), dst)
+    with open(tmp_path / bench.GEMM_COUNTERS["sources"][0], "a") as fh:
+        fh.write("\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_mfma_busy() is None
