@@ -36,12 +36,16 @@ TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight
            "sha256": "afaad22f73bba8a5ec8524b96f2bd8f120989d74e28b40f7071eda13a32da31c",
            "bytes_per_launch": 4578304}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
-# MFMA busy fraction of the prefill GEMM launches at N = 4096 (y only), from
-# rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs)
-# (profiles/gemm_e06_prefill_counters.md); valid only for these sources.
-GEMM_COUNTERS = {"sources": ("ternary_weight_i2_amd/csrc/gemm.hip", "ternary_weight_i2_amd/csrc/common.h"),
-                 "sha256": "dc410ea3ccd9fa2804abd93316db80fe6877ebe45b2e1dbace23b5609ed17934",
-                 "mfma_busy": {"q/k/v": 0.221, "o": 0.149, "gate/up": 0.249, "down": 0.193}}
+# MFMA busy fraction of the prefill GEMM launches (y only), from rocprofv3
+# SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs)
+# (profiles/gemm_e06_prefill_counters.md); valid only for these sources.  At
+# N = 128 the dispatch length under counter collection is mostly the
+# profiler's own per-dispatch cost, so those fractions are lower bounds.
+GEMM_COUNTERS = {"sources": ("ternary_weight_i2_amd/csrc/gemm.hip", "ternary_weight_i2_amd/csrc/gemm_tiles.h",
+                             "ternary_weight_i2_amd/csrc/common.h"),
+                 "sha256": "0df26041d3a3cc12e52a50651b2c95b58714095241e3370776afcd6648cdeed5",
+                 "mfma_busy": {4096: {"q/k/v": 0.227, "o": 0.149, "gate/up": 0.255, "down": 0.193},
+                               128: {"q/k/v": 0.016, "o": 0.008, "gate/up": 0.023, "down": 0.011}}}
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
 
@@ -78,15 +82,17 @@ def measured_traffic():
     return TRAFFIC["bytes_per_launch"] if h.hexdigest() == TRAFFIC["sha256"] else None
 
 
-def measured_mfma_busy():
-    """The recorded MFMA busy fractions of the prefill launches, or None once
-    the GEMM sources changed."""
+def measured_mfma_busy(n_tokens=4096):
+    """The recorded MFMA busy fractions of the prefill launches at this token
+    count, or None once the GEMM sources changed."""
     import hashlib
     h = hashlib.sha256()
     for f in GEMM_COUNTERS["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    return dict(GEMM_COUNTERS["mfma_busy"]) if h.hexdigest() == GEMM_COUNTERS["sha256"] else None
+    if h.hexdigest() != GEMM_COUNTERS["sha256"]:
+        return None
+    return dict(GEMM_COUNTERS["mfma_busy"][n_tokens])
 
 
 def copy_probe():
@@ -646,8 +652,8 @@ def row_prefill(bn, synth, torch, stack):
                              "single": "7 GEMM"}[how],
                 "us": round(t * 1e6, 1), "TOPS": round(ops / t / 1e12, 2),
                 "mfma_frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)}
-            if N == 4096 and tag == "y":
-                rows[f"prefill_N{N}_{tag}"]["mfma_busy_counters"] = measured_mfma_busy()
+            if tag == "y" and how == "group":
+                rows[f"prefill_N{N}_{tag}"]["mfma_busy_counters"] = measured_mfma_busy(N)
             del outs
     return rows
 

@@ -6,8 +6,8 @@
 //
 // Tiling: a workgroup of WM x WN waves computes a BM x BN tile of the output
 // (weight rows x tokens); wave (wm, wn) owns a (32*MI) x (32*NJ) sub-tile made
-// of 32x32 MFMA tiles.  Up to 16 tokens take gemm16_mfma_kernel (below) on
-// the 16x16x64 MFMA instead.
+// of 32x32 MFMA tiles.  Up to 16 tokens take gemm16_mfma_kernel (gemm16.hip)
+// on the 16x16x64 MFMA instead.
 // K advances one 128-weight I2_S block at a time.  One launch may serve
 // several matrices that share the tokens (tiles numbered matrix by matrix).
 //
@@ -38,22 +38,11 @@
 // prefill of a few hundred tokens) a workgroup holds KS groups of WM x WN
 // waves that take alternate blocks of K through their own stages; the
 // groups' int32 partial sums meet in LDS and group 0 writes the tile.
-#include "common.h"
+#include "gemm_tiles.h"
 
 namespace bitnet {
 
-#ifndef BITNET_GEMM_XCD_REMAP
-#define BITNET_GEMM_XCD_REMAP 1   // group each XCD's workgroups on shared token tiles
-#endif
-
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-// Swizzle of the 16-byte pieces of a 128-byte token row in LDS: slot c' of
-// row r holds piece c' ^ tok_swz(r).  A wave's fragment read takes the same
-// piece of 32 consecutive rows; with this mix no two rows among 8 (128-byte
-// bank window) or 16 (256-byte window) consecutive ones share a slot, where
-// r & 7 left rows r and r + 8 on the same banks of a 256-byte window.
-__device__ __forceinline__ int tok_swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 template <int BM, int BN, int WM, int WN, int kStages, int KS>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const GemmArgs a) {
@@ -281,196 +270,6 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
     }
 }
 
-// Up to 16 tokens (batched decode at K >= 8192): 16-token tiles on
-// v_mfma_i32_16x16x64_i8, so no MFMA work is computed and thrown away.  The
-// tokens are the A operand: for step s (64 k each, s = 0, 1) lane l supplies
-// token l%16 at k = 64s + 16*(l/16) + 0..15, a plain 16-byte copy of the
-// staged token row.  The weights are the B operand: lane l takes weight row
-// l%16 of the tile, whose 16 bytes for those k are half (l/16)&1 of the row's
-// 32-byte block slice, field 2s + (l/16)/2 -- one 16-byte LDS read per block
-// serves both steps (shift and mask per dword).  The result register i of
-// lane l holds token 4*(l/16) + i for weight row l%16.  Staging (LDS-DMA, one
-// barrier per block), K groups and the epilogue follow gemm_mfma_kernel.
-template <int BM, int WM, int kStages, int KS>
-__global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArgs a) {
-    static_assert(kStages >= 2 && KS >= 1, "stages, K groups");
-    constexpr int NW = WM;             // waves per K group
-    constexpr int MI = BM / WM / 16;   // 16-row MFMA tiles per wave
-    static_assert(MI >= 1 && BM % (16 * WM) == 0, "tile shape");
-    constexpr int TA = BM / 32, TB = 2, T = TA + TB;   // 1 KB DMA instructions per block
-    static_assert(BM % 32 == 0, "whole 1 KB DMA instructions");
-    constexpr int CMAX = (T + NW - 1) / NW, CMIN = T / NW;
-    static_assert(CMIN >= 1, "every wave issues at least one DMA per block");
-    constexpr int A_BYTES = BM * kBlockBytes, B_BYTES = 16 * kBlock;
-    constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int RED = KS > 1 ? (KS - 1) * NW * MI * 4 * 64 * 4 : 0;
-    static_assert(RED <= KS * kStages * STAGE, "partial sums reuse the staging memory");
-    __shared__ __attribute__((aligned(1024))) int8_t lds_all[KS * kStages * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = (tid >> 6) % NW, grp = (tid >> 6) / NW;
-    int8_t *const lds = lds_all + grp * (kStages * STAGE);
-    const int c16 = lane & 15, g4 = lane >> 4;
-    const int total = (int)gridDim.x;
-    int id = (int)blockIdx.x;
-#if BITNET_GEMM_XCD_REMAP
-    if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
-#endif
-    int mat = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxMats; ++i)
-        if (i < a.nmats && id >= a.mat[i].tile_begin) mat = i;
-    const uint8_t *__restrict__ packed = a.mat[mat].packed;
-    int32_t *__restrict__ dot = a.mat[mat].dot;
-    float *__restrict__ y = a.mat[mat].y;
-    const float alpha = a.mat[mat].alpha;
-    const int M = a.mat[mat].M, K = a.K, N = a.N;
-    const int8_t *__restrict__ xq = a.xq;
-    const int local = id - a.mat[mat].tile_begin;
-    const int mtiles = (M + BM - 1) / BM;
-    const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * 16;
-    const int64_t rowb = K >> 2;
-    const int nkb = K / kBlock;
-    const int nit = (nkb + KS - 1) / KS;
-
-    // DMA sources, as gemm_mfma_kernel (rows and tokens past the end clamped)
-    const bool full = wave < T - CMIN * NW;
-    const int8_t *src[CMAX];
-    int64_t step[CMAX];
-#pragma unroll
-    for (int c = 0; c < CMAX; ++c) {
-        const int j = min(wave + NW * c, T - 1);
-        if (j < TA) {
-            const int row = 32 * j + (lane >> 1);
-            src[c] = reinterpret_cast<const int8_t *>(packed) +
-                     (int64_t)min(m0 + row, M - 1) * rowb + 16 * (lane & 1);
-            step[c] = kBlockBytes;
-        } else {
-            const int row = 8 * (j - TA) + (lane >> 3);
-            const int piece = (lane & 7) ^ tok_swz(row);
-            src[c] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
-            step[c] = kBlock;
-        }
-    }
-    auto issue = [&](int kb, int st) {
-        const int8_t *base = lds + st * STAGE;
-#pragma unroll
-        for (int c = 0; c < CMAX; ++c)
-            if (c < CMIN || full)
-                dma16(src[c] + (int64_t)kb * step[c], lds_addr_of(base + 1024 * (wave + NW * c)));
-    };
-    auto wait_block = [&]() {
-        if (full) wait_vmcnt<CMAX * (kStages - 2)>();
-        else wait_vmcnt<CMIN * (kStages - 2)>();
-    };
-
-    // this lane's four tokens: sum(x) and alpha / s, loaded before the loop
-    int sx[4];
-    float cf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int nc = min(n0 + 4 * g4 + i, N - 1);
-        sx[i] = a.xsum[nc];
-        cf[i] = alpha / a.xs[nc];
-    }
-    v4i acc[MI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) acc[mi] = v4i{0, 0, 0, 0};
-    const int tsw = tok_swz(c16);
-    const int sh0 = 6 - 2 * (g4 >> 1);   // field 2s + g4/2 sits at bit 6 - 2*field
-
-#pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) issue(min(p * KS + grp, nkb - 1), p);
-    for (int it = 0; it < nit; ++it) {
-        wait_block();
-        __syncthreads();
-        issue(min((it + kStages - 1) * KS + grp, nkb - 1), (it + kStages - 1) % kStages);
-        if (KS > 1 && it * KS + grp >= nkb) continue;
-        const int8_t *sa = lds + (it % kStages) * STAGE;
-        const int8_t *sb = sa + A_BYTES;
-        v4i wf[MI], tf[2];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            wf[mi] = *reinterpret_cast<const v4i *>(sa + ((wave * MI + mi) * 16 + c16) * kBlockBytes +
-                                                    16 * (g4 & 1));
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            tf[s2] = *reinterpret_cast<const v4i *>(sb + c16 * kBlock + 16 * ((4 * s2 + g4) ^ tsw));
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int sh = sh0 - 4 * s2;
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const v4i bf = v4i{(wf[mi].x >> sh) & 0x03030303, (wf[mi].y >> sh) & 0x03030303,
-                                   (wf[mi].z >> sh) & 0x03030303, (wf[mi].w >> sh) & 0x03030303};
-                acc[mi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tf[s2], bf, acc[mi], 0, 0, 0);
-            }
-        }
-    }
-    wait_vmcnt<0>();   // drain the trailing re-fetches before the workgroup ends
-    if constexpr (KS > 1) {
-        __syncthreads();
-        int *red = reinterpret_cast<int *>(lds_all);
-        if (grp > 0) {
-            int *dst = red + (((grp - 1) * NW + wave) * MI * 4) * 64 + lane;
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(mi * 4 + e) * 64] = acc[mi][e];
-        }
-        __syncthreads();
-        if (grp > 0) return;
-        for (int gk = 1; gk < KS; ++gk) {
-            const int *srcp = red + (((gk - 1) * NW + wave) * MI * 4) * 64 + lane;
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[mi][e] += srcp[(mi * 4 + e) * 64];
-        }
-    }
-    // lane l: weight row m = tile row + l%16, tokens 4*(l/16) + i; consecutive
-    // lanes write consecutive outputs of a token row
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        const int m = m0 + (wave * MI + mi) * 16 + c16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + 4 * g4 + i;
-            if (m < M && n < N) {
-                const int d = acc[mi][i] - sx[i];
-                const int64_t o = (int64_t)n * M + m;
-                if (dot) dot[o] = d;
-                if (y) y[o] = (float)d * cf[i];
-            }
-        }
-    }
-}
-
-template <int BM, int WM, int S, int KS>
-static hipError_t run_gemm16(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
-                             const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    GemmArgs a{};
-    int64_t tiles = 0;
-    int n = 0;
-    for (int i = 0; i < nmats; ++i) {
-        if (mats[i].M <= 0) continue;
-        a.mat[n] = mats[i];
-        a.mat[n].tile_begin = (int)tiles;
-        tiles += (mats[i].M + BM - 1) / BM;   // one 16-token tile (N <= 16)
-        ++n;
-    }
-    if (n == 0) return hipSuccess;
-    a.nmats = n;
-    a.K = (int)K;
-    a.N = (int)N;
-    a.xq = xq;
-    a.xs = xs;
-    a.xsum = xsum;
-    hipLaunchKernelGGL((gemm16_mfma_kernel<BM, WM, S, KS>), dim3((unsigned)tiles),
-                       dim3(WM * KS * 64), 0, st, a);
-    return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, int S, int KS = 1>
 static hipError_t run_gemm(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                            const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
@@ -513,23 +312,8 @@ hipError_t launch_gemm_mfma(const GemmMat *mats, int nmats, int64_t K, const int
     // 0.6B-class o and down at N = 128: 8.3 -> 7.5 and 9.3 -> 7.4 us); with a
     // threshold of 256 the gate/up launches (192-216 tiles) went 9.5 -> 14.0
     // and 8.2 -> 9.4 us.
-    // Up to 16 tokens (the large layer's batched decode at K >= 8192): 16-token
-    // tiles on the 16x16x64 MFMA, so each block stages 2 KB of tokens instead
-    // of 4 KB for a 32-token tile of which half is padding; 64 rows per tile
-    // where that still gives every CU a workgroup, else 32 (large layer at
-    // N = 16: 987 us per step on 32x32 tiles, 892 on 64x16 with the 32x32
-    // MFMA's second half discarded, 747 on the 16x16x64 MFMA after the
-    // quantiser change).
-    if (N <= 16) {
-        int64_t t64r = 0;
-        for (int i = 0; i < nmats; ++i) t64r += (mats[i].M + 63) / 64;
-        if (t64r >= 256) return run_gemm16<64, 2, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-        // long reductions (the large layer's down projection, K = 28672): K
-        // split over eight wave groups instead of four (877 -> 854 us per step
-        // on the earlier 32-token-wide tiles)
-        if (K >= 16384) return run_gemm16<32, 1, 3, 8>(mats, nmats, K, xq, xs, xsum, N, st);
-        return run_gemm16<32, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
-    }
+    // Up to 16 tokens: 16-token tiles on the 16x16x64 MFMA (gemm16.hip).
+    if (N <= 16) return launch_gemm16(mats, nmats, K, xq, xs, xsum, N, st);
     if (N <= 32) return run_gemm<32, 32, 1, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     int64_t t64 = 0;
     for (int i = 0; i < nmats; ++i) t64 += (mats[i].M + 63) / 64;

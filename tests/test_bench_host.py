@@ -71,7 +71,8 @@ def test_defaults_are_one_gpu(monkeypatch, argv):
 
 
 def test_recorded_mfma_busy_belongs_to_the_committed_gemm(tmp_path, monkeypatch):
-    assert bench.measured_mfma_busy() == bench.GEMM_COUNTERS["mfma_busy"]
+    for n in (128, 4096):
+        assert bench.measured_mfma_busy(n) == bench.GEMM_COUNTERS["mfma_busy"][n]
     for f in bench.GEMM_COUNTERS["sources"]:
         dst = tmp_path / f
         dst.parent.mkdir(parents=True, exist_ok=True)
