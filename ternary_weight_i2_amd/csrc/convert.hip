@@ -44,30 +44,85 @@ __device__ __forceinline__ uint64_t wave_sum_u64c(uint64_t v) {
 }
 
 // Pass 1: the digits of sum |w| over groups of 4 weights g = b*256 + t,
-// g += gridDim*256, normalised into partial[b][0..kMagNorm).  Each digit of a
-// workgroup stays below 2^32 * (weights of the workgroup) < 2^64.
+// g += gridDim*256, normalised into partial[b][0..kMagNorm).
+//
+// Per weight, |w| = m * 2^(P-149) (m < 2^24, P in [0, 253]) goes into one of
+// 16 binary64 buckets, bucket q = P >> 4 holding multiples of 2^(16q-149)
+// below 2^39 of that unit each.  A bucket takes at most 4 * kAbsChunk
+// = 2^13 terms before it is folded, so its sum stays below 2^52 units and
+// every addition is exact in binary64: the bucket sums are exact whatever
+// the order.  Each thread owns its buckets (a column of bk[][] in LDS, added
+// to with LDS float atomics, so no weight waits on the one before); after
+// each chunk it folds them, as integers, into the carry-save digits d of
+// exact_sum.h (each add below 2^37, each digit of a workgroup below 2^64).
+constexpr int kAbsBuckets = 16;
+constexpr int kAbsChunk = 2048;   // groups of 4 weights per thread between folds
+
+__device__ __forceinline__ void abs_bucket_add(double (*bk)[kConvThreads], int tid, float w) {
+    const uint32_t bits = __float_as_uint(w) & 0x7fffffffu;
+    const uint32_t E = bits >> 23;
+    if (E == 0xffu) return;   // non-finite: the pack pass reports it
+    const uint32_t m = E ? ((bits & 0x7fffffu) | 0x800000u) : bits;
+    const int P = E ? (int)E - 1 : 0;
+    __hip_atomic_fetch_add(&bk[P >> 4][tid], ldexp((double)m, P - 149), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void abs_fold(double (*bk)[kConvThreads], int tid, uint64_t *d) {
+#pragma unroll
+    for (int q = 0; q < kAbsBuckets; ++q) {
+        const double t = ldexp(bk[q][tid], 149 - 16 * q);   // an integer below 2^52
+        bk[q][tid] = 0.0;
+        const uint32_t hi = (uint32_t)(t * 0x1p-32);
+        const uint32_t lo = (uint32_t)(t - (double)hi * 0x1p32);
+        const int i = q >> 1;   // bucket unit 2^(16q) = digit i, shifted by 16 (q odd)
+        if (q & 1) {
+            d[i] += (uint64_t)(lo & 0xffffu) << 16;
+            d[i + 1] += (uint64_t)(lo >> 16) + ((uint64_t)hi << 16);
+        } else {
+            d[i] += lo;
+            d[i + 1] += hi;
+        }
+    }
+}
+
 template <int BF16>
 __global__ __launch_bounds__(kConvThreads) void absmean_partial_kernel(
     const void *__restrict__ w, int64_t n4, uint32_t *__restrict__ partial) {
+    __shared__ double bk[kAbsBuckets][kConvThreads];
     __shared__ uint64_t red[kConvThreads / 64][kMagDigits];
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < kAbsBuckets; ++q) bk[q][tid] = 0.0;
     uint64_t d[kMagDigits];
 #pragma unroll
     for (int i = 0; i < kMagDigits; ++i) d[i] = 0;
-    for (int64_t g = (int64_t)blockIdx.x * kConvThreads + threadIdx.x; g < n4;
-         g += (int64_t)gridDim.x * kConvThreads) {
-        float v[4];
-        load4<BF16>(w, g, v);
+    const int64_t stride = (int64_t)gridDim.x * kConvThreads;
+    int64_t g = (int64_t)blockIdx.x * kConvThreads + tid;
+    while (g < n4) {
+        const int64_t gend = min(n4, g + (int64_t)kAbsChunk * stride);
+        for (; g < gend; g += 4 * stride) {
+            // four groups in flight (clamped addresses; only those below gend count)
+            float v[4][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mag_add(d, v[e]);
+            for (int u = 0; u < 4; ++u) load4<BF16>(w, min(g + u * stride, n4 - 1), v[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (g + u * stride < gend) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) abs_bucket_add(bk, tid, v[u][e]);
+                }
+        }
+        abs_fold(bk, tid, d);
     }
 #pragma unroll
     for (int i = 0; i < kMagDigits; ++i) d[i] = wave_sum_u64c(d[i]);
-    if ((threadIdx.x & 63) == 0) {
+    if ((tid & 63) == 0) {
 #pragma unroll
-        for (int i = 0; i < kMagDigits; ++i) red[threadIdx.x >> 6][i] = d[i];
+        for (int i = 0; i < kMagDigits; ++i) red[tid >> 6][i] = d[i];
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         uint64_t t[kMagDigits];
         for (int i = 0; i < kMagDigits; ++i) {
             t[i] = 0;
@@ -78,29 +133,33 @@ __global__ __launch_bounds__(kConvThreads) void absmean_partial_kernel(
 }
 
 // Pass 2 (one workgroup, a thread per partial): the exact total, rounded once
-// to binary64; alpha = max(fp32(sum / n), 1e-5).
+// to binary64; alpha = max(fp32(sum / n), 1e-5).  The partials' digits are
+// transposed through LDS so that wave i adds digit i of every partial (16
+// reads per lane and one wave reduction per digit, in parallel).
 __global__ __launch_bounds__(1024) void absmean_final_kernel(
     const uint32_t *__restrict__ partial, int nparts, int64_t n, float *__restrict__ alpha) {
-    __shared__ uint64_t red[16][kMagNorm];
-    uint64_t d[kMagNorm];
+    static_assert(kMagNorm <= 1024 / 64, "a wave per digit");
+    __shared__ uint32_t col[kMagNorm][1024];
+    __shared__ uint64_t tot[kMagNorm];
+    const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
 #pragma unroll
     for (int i = 0; i < kMagNorm; ++i)
-        d[i] = (int)threadIdx.x < nparts ? partial[(int64_t)threadIdx.x * kMagNorm + i] : 0;
+        col[i][t] = t < nparts ? partial[(int64_t)t * kMagNorm + i] : 0u;
+    __syncthreads();
+    if (wv < kMagNorm) {
+        uint64_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < kMagNorm; ++i) d[i] = wave_sum_u64c(d[i]);
-    if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-        for (int i = 0; i < kMagNorm; ++i) red[threadIdx.x >> 6][i] = d[i];
+        for (int j = 0; j < 1024 / 64; ++j) sum += col[wv][lane + 64 * j];
+        sum = wave_sum_u64c(sum);
+        if (lane == 0) tot[wv] = sum;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t t[kMagNorm];
-        for (int i = 0; i < kMagNorm; ++i) {
-            t[i] = 0;
-            for (int wv = 0; wv < 16; ++wv) t[i] += red[wv][i];
-        }
+    if (t == 0) {
+        uint64_t d[kMagNorm];
+#pragma unroll
+        for (int i = 0; i < kMagNorm; ++i) d[i] = tot[i];
         uint32_t nd[kMagNorm];
-        mag_normalise(t, kMagNorm, nd);
+        mag_normalise(d, kMagNorm, nd);
         const double s = mag_round(nd);
         const float a = (float)(s / (double)n);
         *alpha = a > 1e-5f ? a : 1e-5f;

@@ -19,10 +19,12 @@
 //    cannot carry into the round bit, the level-1 integer decides the
 //    rounding; otherwise further levels add the next kWin bits of every
 //    square into an exact big integer until no square has bits left below.
-//  * Digit sums (magnitudes).  |w| = m * 2^P' in units of 2^-149, P' in
-//    [0, 253], m < 2^24: added into nine 32-bit digits held in 64-bit lanes
-//    (carry-save; no carries while accumulating), which covers every finite
-//    fp32 with no window and no second level.
+//  * Digit sums (magnitudes).  Nine 32-bit digits held in 64-bit lanes, in
+//    units of 2^-149 (carry-save; no carries while accumulating), cover every
+//    finite fp32 |w| = m * 2^P' (P' in [0, 253], m < 2^24) with no window and
+//    no second level.  The AbsMean kernel gathers the magnitudes in exact
+//    binary64 buckets first and folds those into the digits (convert.hip);
+//    mag_normalise and mag_round turn digit sums into one binary64 value.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -259,22 +261,6 @@ __host__ __device__ __forceinline__ double big_round(const uint32_t *big, int b)
 constexpr int kMagDigits = 9;     // 288 bits >= 24 + 253
 constexpr int kMagNorm = 12;      // normalised digits of a (workgroup or total) sum
 
-// |w| into the carry-save digits d[0..8] (units 2^-149); non-finite ignored.
-__host__ __device__ __forceinline__ void mag_add(uint64_t *d, float w) {
-    uint32_t bits;
-    __builtin_memcpy(&bits, &w, 4);
-    bits &= 0x7fffffffu;
-    const uint32_t E = bits >> 23;
-    if (E == 0xffu) return;
-    const uint64_t m = E ? ((bits & 0x7fffffu) | 0x800000u) : (bits & 0x7fffffu);
-    const int P = E ? (int)E - 1 : 0;
-    const int q = P >> 5;
-    const uint64_t t = m << (P & 31);
-    const uint64_t lo = t & 0xffffffffu, hi = t >> 32;
-#pragma unroll
-    for (int i = 0; i < kMagDigits; ++i) d[i] += (q == i ? lo : 0) + (q + 1 == i ? hi : 0);
-}
-
 // Carry-save digits (each < 2^64) -> normalised 32-bit digits.
 __host__ __device__ __forceinline__ void mag_normalise(const uint64_t *d, int nd, uint32_t *out) {
     uint64_t carry = 0;
@@ -288,20 +274,40 @@ __host__ __device__ __forceinline__ void mag_normalise(const uint64_t *d, int nd
 
 // Normalised digits (units 2^-149) rounded once to binary64.
 __host__ __device__ __forceinline__ double mag_round(const uint32_t *n) {
-    int top = -1;
-    for (int i = kMagNorm - 1; i >= 0 && top < 0; --i)
-        if (n[i]) top = 32 * i + 31 - __builtin_clz(n[i]);
-    if (top < 0) return 0.0;
-    auto bit = [&](int i) { return (int)((n[i >> 5] >> (i & 31)) & 1u); };
-    uint64_t keep = 0;
-    const int lo = top - 52;
-    for (int i = top; i >= lo && i >= 0; --i) keep = 2 * keep + (uint64_t)bit(i);
-    if (lo <= 0) return __builtin_ldexp((double)keep, -149);
-    const int rb = bit(lo - 1);
-    int sticky = 0;
-    for (int i = lo - 2; i >= 0 && !sticky; --i) sticky = bit(i);
+    // Word-level: the top three words form a 96-bit window W (bit 0 of W has
+    // weight 2^(32*(ti-2)-149); words below index 0 count as zero), of which
+    // the 53 bits from W's top bit are kept; the round bit and the sticky bit
+    // (the rest of W and every lower word) decide round-to-nearest-even.
+    // Every index below is a compile-time one (unrolled), so nothing goes to
+    // scratch memory.
+    int ti = -1;
+#pragma unroll
+    for (int i = 0; i < kMagNorm; ++i)
+        if (n[i]) ti = i;
+    if (ti < 0) return 0.0;
+    uint32_t w2 = 0, w1 = 0, w0 = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < kMagNorm; ++i) {
+        if (i == ti) w2 = n[i];
+        if (i == ti - 1) w1 = n[i];
+        if (i == ti - 2) w0 = n[i];
+        if (i < ti - 2) below |= n[i];
+    }
+    const uint64_t hi = (uint64_t)w2 << 32 | w1;
+    const int s = 95 - __builtin_clz(w2) - 52;   // low bits of W dropped: 12..43
+    uint64_t keep;
+    int rb, sticky;
+    if (s <= 32) {
+        keep = (hi << (32 - s)) | ((uint64_t)w0 >> s);
+        rb = (int)((w0 >> (s - 1)) & 1u);
+        sticky = (s > 1 && (w0 & ((1u << (s - 1)) - 1u)) != 0) || below != 0;
+    } else {
+        keep = hi >> (s - 32);
+        rb = (int)((hi >> (s - 33)) & 1u);
+        sticky = (s > 33 && (hi & ((1ull << (s - 33)) - 1ull)) != 0) || w0 != 0 || below != 0;
+    }
     if (rb && (sticky || (keep & 1u))) ++keep;
-    return __builtin_ldexp((double)keep, lo - 149);
+    return __builtin_ldexp((double)keep, 32 * (ti - 2) + s - 149);
 }
 
 }  // namespace bitnet
