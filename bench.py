@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "afaad22f73bba8a5ec8524b96f2bd8f120989d74e28b40f7071eda13a32da31c",
+           "sha256": "cf0ee7b2e16ac917dc6e2ed4b4cf441f2b022ba4460ef57863f166e4f793552c",
            "bytes_per_launch": 4578304}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 # MFMA busy fraction of the prefill GEMM launches (y only), from rocprofv3
@@ -161,6 +161,43 @@ def run_step_unfused(bn, stack):
             bn.quant_act(x, out=(xq, xs, xsum))
             for P, alpha, dot, y, M, K in mats:
                 bn.gemv(P, alpha, xq, xs, xsum, out=(dot, y))
+
+
+def kernel_only(bn, torch, stack, step_bytes_total, launches, replays=5):
+    """Each launch's own duration -- its first workgroup's start to its last
+    wave's end, s_memrealtime stamps (100 MHz) recorded by the instrumented
+    build of the same sources (libbitnet_i2s_stamps.so) -- over a few replays
+    of the same captured step: no tracer serialises the launches and the
+    gaps between them are left out.  None if that build is missing."""
+    try:
+        bn.use_library("stamps")
+    except RuntimeError:
+        return None
+    try:
+        bn.stamps_reset(rewind=True)
+        g = capture(torch, lambda: run_step(bn, stack))   # warm call + capture take 2 x launches slots
+        for _ in range(5):
+            g.replay()
+        dur, spans = [], []
+        for _ in range(replays):
+            bn.stamps_reset(rewind=False)
+            g.replay()
+            pairs = bn.stamps_read(2 * launches)[-launches:]
+            dur += [(e - s) * 0.01 for s, e in pairs]
+            spans.append((max(e for _, e in pairs) - min(s for s, _ in pairs)) * 0.01)
+        del g
+    finally:
+        bn.use_library("main")
+    dur.sort()
+    mean = sum(dur) / len(dur)
+    return {"mean_us": round(mean, 3), "p10_us": round(dur[len(dur) // 10], 2),
+            "p50_us": round(dur[len(dur) // 2], 2), "p90_us": round(dur[len(dur) * 9 // 10], 2),
+            "achieved_GBs": round(step_bytes_total / launches / (mean * 1e-6) / 1e9, 1),
+            "step_span_us": round(sum(spans) / len(spans), 2), "launches": launches,
+            "replays": replays,
+            "method": "first-workgroup start to last-wave end per launch, s_memrealtime stamps "
+                      "(10 ns ticks) from libbitnet_i2s_stamps.so, the same sources built with "
+                      "-DBITNET_STAMPS; graph replays of the same step"}
 
 
 def capture(torch, fn):
@@ -713,6 +750,7 @@ def main():
     single.sort()
     pct = {f"p{q}": round(single[int(q / 100 * (len(single) - 1))], 4) for q in (10, 50, 90)}
     context = device_context(torch)
+    konly = kernel_only(bn, torch, stack, sbytes, launches)
 
     # context: the same work through the unfused calls, in a graph, and eager
     g_unf = capture(torch, lambda: run_step_unfused(bn, stack))
@@ -757,7 +795,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(per_launch_s * 1e6, 3),
                      "avg_launch_method": "step time / launches per step (HIP events on the "
-                                          "replay stream; includes the gaps between launches)"},
+                                          "replay stream; includes the gaps between launches)",
+                     "kernel_only": konly},
         "cpu_baseline": cpu,
         "single_step_ms": pct,
         "context": context,

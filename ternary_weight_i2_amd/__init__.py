@@ -8,4 +8,5 @@ is missing -- there is no fallback path.
 from ._binding import (  # noqa: F401
     BitnetError, I2SMatrix, abi_version, absmean_pack, ffn, ffn_act_quant, gemm, gemm_group,
     gemv, gemv_group, gemv_lut, lib_path, linear, load, pack, pack_f32, quant_act,
+    stamps_read, stamps_reset, use_library,
 )

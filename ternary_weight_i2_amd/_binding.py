@@ -14,6 +14,9 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbitnet_i2s.so")
+# the same library built with per-launch start/end stamps of the decode GEMV
+# (include/bitnet_i2s_stamps.h); a measurement aid, never loaded by default
+_STAMPS_PATH = os.path.join(_HERE, "libbitnet_i2s_stamps.so")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_VALUE, E_HIP = range(7)
 F32, BF16 = 0, 1
@@ -49,11 +52,49 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    _lib = _open(_LIB_PATH)
+    return _lib
+
+
+def use_library(which: str) -> None:
+    """Route every call through the product library ("main") or its
+    instrumented twin ("stamps", which also records per-launch start/end
+    stamps of the decode GEMV).  Both must have been built."""
+    global _lib
+    if which == "main":
+        _lib = _open(_LIB_PATH)
+    elif which == "stamps":
+        L = _open(_STAMPS_PATH)
+        L.bitnet_stamps_reset.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.bitnet_stamps_reset.restype = ctypes.c_int
+        L.bitnet_stamps_read.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.c_int]
+        L.bitnet_stamps_read.restype = ctypes.c_int
+        _lib = L
+    else:
+        raise ValueError(which)
+
+
+def stamps_reset(rewind: bool = False) -> None:
+    """Clear the stamp slots on the current stream (instrumented library)."""
+    import torch
+    _check(load().bitnet_stamps_reset(int(rewind), torch.cuda.current_stream().cuda_stream))
+
+
+def stamps_read(max_launches: int) -> list[tuple[int, int]]:
+    """[(start, end)] in 100 MHz ticks for the launches since the last rewind."""
+    buf = (ctypes.c_uint64 * (2 * max_launches))()
+    n = load().bitnet_stamps_read(buf, max_launches)
+    if n < 0:
+        raise BitnetError(E_HIP, "bitnet_stamps_read failed")
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+            f"{path} is missing: build it with __graft_entry__.build() "
             "(there is no fallback implementation)")
-    L = ctypes.CDLL(_LIB_PATH)
+    L = ctypes.CDLL(path)
     p, i64, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
     L.bitnet_pack_i2s.argtypes = [p, i64, i64, p, p]
     L.bitnet_quant_act_i8.argtypes = [p, ctypes.c_int, i64, i64, p, p, p, p]
@@ -81,7 +122,6 @@ def load() -> ctypes.CDLL:
     L.bitnet_abi_version.argtypes = []
     L.bitnet_last_error.argtypes = []
     L.bitnet_last_error.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbitnet_i2s.so")
+OUT_STAMPS = os.path.join(HERE, "libbitnet_i2s_stamps.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -42,20 +43,27 @@ def _run(cmd: list[str], verbose: bool) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile each translation unit in parallel, then link the shared library."""
+    """Compile each translation unit in parallel, then link the shared
+    library and its instrumented twin (-DBITNET_STAMPS: per-launch start/end
+    stamps of the decode GEMV, include/bitnet_i2s_stamps.h)."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     srcs = sources()
+    variants = ((OUT, []), (OUT_STAMPS, ["-DBITNET_STAMPS"]))
     with tempfile.TemporaryDirectory(prefix="bitnet_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
-        jobs = [[HIPCC, *FLAGS, *inc, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        jobs, objs = [], []
+        for vi, (_, defs) in enumerate(variants):
+            vo = [os.path.join(tmpdir, f"{vi}_" + os.path.basename(s)[:-4] + ".o") for s in srcs]
+            jobs += [[HIPCC, *FLAGS, *defs, *inc, "-c", s, "-o", o] for s, o in zip(srcs, vo)]
+            objs.append(vo)
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), jobs))
-        tmp = OUT + ".tmp"
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, OUT)
+        for (out, _), vo in zip(variants, objs):
+            tmp = out + ".tmp"
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *vo, "-o", tmp], verbose)
+            os.replace(tmp, out)
     return OUT
 
 

@@ -451,3 +451,22 @@ BITNET_API int bitnet_linear_i2s(const void *x, int dtype, int64_t N, int64_t K,
     return linear_impl("bitnet_linear_i2s", x, dtype, N, K, mats, n_mats, xq, x_scale, x_sum,
                        stream);
 }
+
+#ifdef BITNET_STAMPS
+// Instrumented build only (include/bitnet_i2s_stamps.h).
+namespace bitnet {
+int stamps_reset(int rewind, hipStream_t st);
+int stamps_read(unsigned long long *out, int max_launches);
+}  // namespace bitnet
+
+BITNET_API int bitnet_stamps_reset(int rewind, void *stream) {
+    if (bitnet::stamps_reset(rewind, static_cast<hipStream_t>(stream)) != 0)
+        return fail(BITNET_E_HIP, "bitnet_stamps_reset: no stamp slots on this device");
+    return ok();
+}
+
+BITNET_API int bitnet_stamps_read(uint64_t *out, int max_launches) {
+    if (!out && max_launches > 0) return -1;
+    return bitnet::stamps_read(reinterpret_cast<unsigned long long *>(out), max_launches);
+}
+#endif

@@ -2,6 +2,8 @@
 // launch geometry (the kernel template is in gemv_valu.h).
 #include "gemv_valu.h"
 
+#include <vector>
+
 namespace bitnet {
 
 // Lanes per row (a power of two in {8,16,32,64}; each lane then takes
@@ -65,6 +67,76 @@ static GemvGeometry gemv_geometry(int64_t K, int64_t total_rows, int mode) {
     return g;
 }
 
+#ifdef BITNET_STAMPS
+// Launch slots of the instrumented build, taken in launch order (at capture
+// time for a captured graph) and wrapping after kStampSlots launches.  A slot
+// is kStampSubs sub-slots on 128-byte lines of their own ([start, end] in
+// the first 16 bytes); workgroup b stamps sub-slot b % kStampSubs, so the
+// atomics of one launch spread over 64 lines instead of queueing on one.
+constexpr int kStampSlots = 512;
+constexpr int kStampStride = 16;   // unsigned long longs per sub-slot (128 bytes)
+constexpr int kStampSlotLen = kStampSubs * kStampStride;
+__device__ unsigned long long g_stamps[kStampSlots * kStampSlotLen];
+static unsigned long long *g_stamps_addr[64];
+static int g_stamp_next = 0;
+
+static unsigned long long *stamps_base() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (!g_stamps_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_stamps)) != hipSuccess) return nullptr;
+        g_stamps_addr[dev] = static_cast<unsigned long long *>(p);
+    }
+    return g_stamps_addr[dev];
+}
+
+unsigned long long *stamp_slot() {
+    unsigned long long *b = stamps_base();
+    return b ? b + (size_t)(g_stamp_next++ % kStampSlots) * kStampSlotLen : nullptr;
+}
+
+__global__ void stamps_clear_kernel(unsigned long long *s) {
+    const int i = blockIdx.x * 256 + threadIdx.x;   // sub-slot
+    if (i < kStampSlots * kStampSubs) {
+        s[(size_t)i * kStampStride] = ~0ull;
+        s[(size_t)i * kStampStride + 1] = 0ull;
+    }
+}
+
+int stamps_reset(int rewind, hipStream_t st) {
+    unsigned long long *b = stamps_base();
+    if (!b) return -1;
+    if (rewind) g_stamp_next = 0;
+    hipLaunchKernelGGL(stamps_clear_kernel, dim3(kStampSlots * kStampSubs / 256), dim3(256), 0, st, b);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// [min start, max end] over the sub-slots of each launch since the rewind
+int stamps_read(unsigned long long *out, int max_launches) {
+    unsigned long long *b = stamps_base();
+    if (!b || max_launches < 0) return -1;
+    int n = g_stamp_next < kStampSlots ? g_stamp_next : kStampSlots;
+    if (n > max_launches) n = max_launches;
+    if (hipDeviceSynchronize() != hipSuccess) return -1;
+    std::vector<unsigned long long> h((size_t)n * kStampSlotLen);
+    if (n && hipMemcpy(h.data(), b, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost) !=
+                 hipSuccess)
+        return -1;
+    for (int i = 0; i < n; ++i) {
+        unsigned long long lo = ~0ull, hi = 0;
+        for (int j = 0; j < kStampSubs; ++j) {
+            const unsigned long long *q = &h[(size_t)i * kStampSlotLen + (size_t)j * kStampStride];
+            if (q[0] < lo) lo = q[0];
+            if (q[1] > hi) hi = q[1];
+        }
+        out[2 * i] = lo;
+        out[2 * i + 1] = hi;
+    }
+    return n;
+}
+#endif
+
 hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N,
                             int mode, const void *x, const float *xs,
                             const int32_t *xsum, int8_t *xq_out, float *xs_out,
@@ -77,7 +149,7 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
     const int esize = mode == 0 ? 1 : (mode == 1 ? 4 : 2);
     for (int64_t n0 = 0; n0 < N; n0 += per) {
         const int nt = (int)((N - n0) < per ? (N - n0) : per);
-        GemvArgs a{};
+        GemvKernelArgs a{};
         int wg = 0;
         for (int i = 0; i < nmats; ++i) {
             a.mat[i] = mats[i];
@@ -100,6 +172,9 @@ hipError_t launch_gemv_valu(const GemvMat *mats, int nmats, int64_t K, int64_t N
             a.xsum_out = xsum_out ? xsum_out + n0 : nullptr;
         }
         if (wg == 0) continue;
+#ifdef BITNET_STAMPS
+        a.stamp = stamp_slot();
+#endif
         hipError_t e;
         const unsigned g = (unsigned)wg;
         // J <= 4: short-row kernels with exactly 3 or 4 chunk slots

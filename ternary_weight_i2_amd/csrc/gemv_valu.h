@@ -240,8 +240,22 @@ struct TokenPrologue {
 // chunk loop has no run-time guard (chunks past J carry zeroed weights), so
 // the compiler can issue every chunk's LDS reads at once -- the tail after the
 // weights arrive is a latency chain in these small launches.
+// The instrumented build (-DBITNET_STAMPS, libbitnet_i2s_stamps.so) gives
+// every launch a slot that receives the first wave's start and the last
+// wave's end (s_memrealtime ticks, 100 MHz) by atomic min / max, so a launch's
+// own duration can be read without a tracer.  The product build has no slot.
+#ifdef BITNET_STAMPS
+constexpr int kStampSubs = 64;   // sub-slots per launch (workgroup b takes b % 64)
+struct GemvKernelArgs : GemvArgs {
+    unsigned long long *stamp;   // this launch's slot (kStampSubs lines of 128 bytes), or null
+};
+unsigned long long *stamp_slot();   // gemv.hip: the slot of the next launch
+#else
+using GemvKernelArgs = GemvArgs;
+#endif
+
 template <int NT, int LPR, int MODE, int JM, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelArgs a) {
     constexpr int kThreads = WAVES * 64;
     constexpr bool kAllChunks = JM <= 4;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
@@ -253,6 +267,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a)
     __shared__ int redi[WAVES][NT];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#ifdef BITNET_STAMPS
+    // start: thread 0 of each workgroup; end: the workgroup's last wave to
+    // finish (an LDS count), so a workgroup makes two global atomics
+    unsigned long long *const stamp = a.stamp ? a.stamp + 16 * (blockIdx.x % kStampSubs) : nullptr;
+    __shared__ int stamp_waves;
+    if (tid == 0) {
+        stamp_waves = 0;
+        if (stamp) atomicMin(stamp, __builtin_amdgcn_s_memrealtime());
+    }
+#endif
     const int sub = lane / LPR, u = lane % LPR;
     int mi = 0;
 #pragma unroll
@@ -407,12 +431,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvArgs a)
         load_group(g, cur);
         compute(g, cur);
     }
+#ifdef BITNET_STAMPS
+    if (stamp && lane == 0 && atomicAdd(&stamp_waves, 1) == WAVES - 1)
+        atomicMax(stamp + 1, __builtin_amdgcn_s_memrealtime());
+#endif
 }
 
 // One launch of the kernel for NT tokens per pass, token mode MODE and the
 // lane count chosen by the host.
 template <int NT, int MODE, int JM>
-static hipError_t launch_gemv_ntj(const GemvArgs &a, int lpr, unsigned grid, hipStream_t st) {
+static hipError_t launch_gemv_ntj(const GemvKernelArgs &a, int lpr, unsigned grid, hipStream_t st) {
     const size_t lds = (size_t)a.ntok * (size_t)a.K;
     const dim3 b(kGemvWaves * 64);
     switch (lpr) {
@@ -429,7 +457,7 @@ static hipError_t launch_gemv_ntj(const GemvArgs &a, int lpr, unsigned grid, hip
 // long: 16 waves of 64 lanes per row).  Each (NT, MODE) pair is
 // instantiated in one of the gemv_valu_n*.hip translation units.
 template <int NT, int MODE>
-hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, bool long_rows,
+hipError_t launch_gemv_nt(const GemvKernelArgs &a, int lpr, int short_j, bool long_rows,
                           unsigned grid, hipStream_t st) {
     if (long_rows) {
         const size_t lds = (size_t)a.ntok * (size_t)a.K;
@@ -445,7 +473,7 @@ hipError_t launch_gemv_nt(const GemvArgs &a, int lpr, int short_j, bool long_row
 }
 
 #define BITNET_GEMV_EXTERN(NT, MODE) \
-    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvArgs &, int, int, bool, unsigned, \
+    extern template hipError_t launch_gemv_nt<NT, MODE>(const GemvKernelArgs &, int, int, bool, unsigned, \
                                                         hipStream_t)
 // passes of one or two tokens (larger batches run on MFMA)
 BITNET_GEMV_EXTERN(1, 0); BITNET_GEMV_EXTERN(1, 1); BITNET_GEMV_EXTERN(1, 2);

@@ -3,7 +3,7 @@
 #include "gemv_valu.h"
 
 namespace bitnet {
-template hipError_t launch_gemv_nt<1, 0>(const GemvArgs &, int, int, bool, unsigned, hipStream_t);
-template hipError_t launch_gemv_nt<1, 1>(const GemvArgs &, int, int, bool, unsigned, hipStream_t);
-template hipError_t launch_gemv_nt<1, 2>(const GemvArgs &, int, int, bool, unsigned, hipStream_t);
+template hipError_t launch_gemv_nt<1, 0>(const GemvKernelArgs &, int, int, bool, unsigned, hipStream_t);
+template hipError_t launch_gemv_nt<1, 1>(const GemvKernelArgs &, int, int, bool, unsigned, hipStream_t);
+template hipError_t launch_gemv_nt<1, 2>(const GemvKernelArgs &, int, int, bool, unsigned, hipStream_t);
 }  // namespace bitnet

@@ -13,6 +13,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitnet_i2s.h")
+STAMPS_HEADER = os.path.join(ROOT, "include", "bitnet_i2s_stamps.h")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_VALUE, E_HIP = range(7)
 FAKE = 0x10000          # 64 KiB-aligned non-null value, never dereferenced
@@ -25,8 +26,8 @@ def L():
     return _binding.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(bitnet_\w+)\s*\(", text, flags=re.M)
 
@@ -44,6 +45,19 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for fn in declared_functions():
         assert hasattr(L, fn), fn
+
+
+def test_stamps_build_exports_both_headers_and_the_product_build_neither(L):
+    """The instrumented twin exports the whole ABI plus the stamp calls; the
+    product library has no stamp calls."""
+    from ternary_weight_i2_amd import _binding
+    S = ctypes.CDLL(_binding._STAMPS_PATH)
+    stamps = declared_functions(STAMPS_HEADER)
+    assert set(stamps) == {"bitnet_stamps_reset", "bitnet_stamps_read"}
+    for fn in declared_functions() + stamps:
+        assert hasattr(S, fn), fn
+    for fn in stamps:
+        assert not hasattr(L, fn), fn
 
 
 def test_abi_version(L):
