@@ -183,6 +183,15 @@ def test_gemv_small(bn, M, K, N):
     run_case(bn, M, K, N, "gemv", seed=M * 131 + K + N)
 
 
+# int8 tokens longer than two 16-byte pieces per thread (staged to LDS before
+# the weights are loaded), one and two tokens, ragged M, K up to 32768
+@pytest.mark.parametrize("M,K,N", [(300, 28672, 1), (300, 28672, 2), (4100, 32768, 1),
+                                   (129, 8192, 2), (130, 12288, 1), (70, 9216, 1),
+                                   (65, 20480, 2)])
+def test_gemv_long_int8_tokens(bn, M, K, N):
+    run_case(bn, M, K, N, "gemv", seed=M + K + N)
+
+
 @pytest.mark.parametrize("M,K,N", SMALL + [(200, 1024, 128), (77, 640, 300), (300, 256, 129)])
 def test_gemm_small(bn, M, K, N):
     run_case(bn, M, K, N, "gemm", seed=M * 17 + K * 3 + N)
