@@ -2,7 +2,11 @@
 // launch geometry (the kernel template is in gemv_valu.h).
 #include "gemv_valu.h"
 
+#ifdef BITNET_STAMPS
+#include <atomic>
+#include <mutex>
 #include <vector>
+#endif
 
 namespace bitnet {
 
@@ -78,11 +82,13 @@ constexpr int kStampStride = 16;   // unsigned long longs per sub-slot (128 byte
 constexpr int kStampSlotLen = kStampSubs * kStampStride;
 __device__ unsigned long long g_stamps[kStampSlots * kStampSlotLen];
 static unsigned long long *g_stamps_addr[64];
-static int g_stamp_next = 0;
+static std::mutex g_stamps_mu;
+static std::atomic<int> g_stamp_next{0};
 
 static unsigned long long *stamps_base() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(g_stamps_mu);
     if (!g_stamps_addr[dev]) {
         void *p = nullptr;
         if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_stamps)) != hipSuccess) return nullptr;
@@ -107,7 +113,7 @@ __global__ void stamps_clear_kernel(unsigned long long *s) {
 int stamps_reset(int rewind, hipStream_t st) {
     unsigned long long *b = stamps_base();
     if (!b) return -1;
-    if (rewind) g_stamp_next = 0;
+    if (rewind) g_stamp_next.store(0);
     hipLaunchKernelGGL(stamps_clear_kernel, dim3(kStampSlots * kStampSubs / 256), dim3(256), 0, st, b);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -116,7 +122,8 @@ int stamps_reset(int rewind, hipStream_t st) {
 int stamps_read(unsigned long long *out, int max_launches) {
     unsigned long long *b = stamps_base();
     if (!b || max_launches < 0) return -1;
-    int n = g_stamp_next < kStampSlots ? g_stamp_next : kStampSlots;
+    const int used = g_stamp_next.load();
+    int n = used < kStampSlots ? used : kStampSlots;
     if (n > max_launches) n = max_launches;
     if (hipDeviceSynchronize() != hipSuccess) return -1;
     std::vector<unsigned long long> h((size_t)n * kStampSlotLen);
