@@ -195,24 +195,32 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 // thread issues the loads of all its R 16-byte pieces at once (clamped,
 // always-valid addresses; a repeated last piece cannot change the absmax and
 // is not emitted), so a token costs one memory round trip instead of one per
-// piece and pass.  Identical arithmetic, identical bits.
-template <int BF16, int R>
+// piece and pass.  Short rows (at most 64 or 128 pieces) share a workgroup:
+// TPB tokens, kQuantThreads / TPB threads each, so no thread idles.
+// Identical arithmetic, identical bits.
+template <int BF16, int R, int TPB>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
-    const void *__restrict__ x, int64_t K, int8_t *__restrict__ xq,
+    const void *__restrict__ x, int64_t N, int64_t K, int8_t *__restrict__ xq,
     float *__restrict__ xs, int32_t *__restrict__ xsum) {
     using V = Vec16<BF16>;
     constexpr int E = V::kElems;
+    constexpr int T = kQuantThreads / TPB;   // threads per token
+    constexpr int TW = T / 64;               // waves per token
+    static_assert(TW >= 1 && TPB * TW == kQuantWaves, "whole waves per token");
     __shared__ float red_f[kQuantWaves];
     __shared__ int red_i[kQuantWaves];
-    const int64_t n = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int slot = tid / T, lt = tid - slot * T;   // this thread's token in the block
+    const int64_t nb = (int64_t)blockIdx.x * TPB + slot;
+    const bool valid = nb < N;                       // a ragged last block: loads stay in bounds
+    const int64_t n = valid ? nb : N - 1;
     const char *row = reinterpret_cast<const char *>(x) + n * K * (BF16 ? 2 : 4);
     const int nvec = (int)(K / E);
 
     uint4 raw[R];   // the pieces as loaded; widened where used
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        raw[r] = reinterpret_cast<const uint4 *>(row)[min(tid + r * kQuantThreads, nvec - 1)];
+        raw[r] = reinterpret_cast<const uint4 *>(row)[min(lt + r * T, nvec - 1)];
     float a = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -224,16 +232,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
     a = wave_max_f32(a);
     if (lane == 0) red_f[wv] = a;
     __syncthreads();
-    a = red_f[0];
+    a = red_f[slot * TW];
 #pragma unroll
-    for (int w = 1; w < kQuantWaves; ++w) a = fmaxf(a, red_f[w]);
+    for (int w = 1; w < TW; ++w) a = fmaxf(a, red_f[slot * TW + w]);
     const float s = quant_scale(a);
 
     int8_t *qrow = xq + n * K;
     int sum = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int i = tid + r * kQuantThreads;
+        const int i = lt + r * T;
         if (i < nvec) {
             float v[E];
             V::widen(raw[r], v);
@@ -246,21 +254,23 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
                 sum += qi;
                 packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
             }
-            if (E == 8) {
-                reinterpret_cast<uint2 *>(qrow)[i] = make_uint2(packedq[0], packedq[E / 4 - 1]);
-            } else {
-                reinterpret_cast<uint32_t *>(qrow)[i] = packedq[0];
+            if (valid) {
+                if (E == 8) {
+                    reinterpret_cast<uint2 *>(qrow)[i] = make_uint2(packedq[0], packedq[E / 4 - 1]);
+                } else {
+                    reinterpret_cast<uint32_t *>(qrow)[i] = packedq[0];
+                }
             }
         }
     }
     sum = wave_sum_i32(sum);
     if (lane == 0) red_i[wv] = sum;
     __syncthreads();
-    if (tid == 0) {
+    if (lt == 0 && valid) {
         xs[n] = s;
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < kQuantWaves; ++w) t += red_i[w];
+        for (int w = 0; w < TW; ++w) t += red_i[slot * TW + w];
         xsum[n] = t;
     }
 }
@@ -268,13 +278,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
 template <int BF16>
 static hipError_t launch_quant_t(const void *x, int64_t N, int64_t K, int8_t *xq, float *xs,
                                  int32_t *xsum, hipStream_t st) {
-    const int64_t per = (K / Vec16<BF16>::kElems + kQuantThreads - 1) / kQuantThreads;
+    const int64_t pieces = K / Vec16<BF16>::kElems;
+    const int64_t per = (pieces + kQuantThreads - 1) / kQuantThreads;
     const dim3 g((unsigned)N), b(kQuantThreads);
-    if (per <= 1) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1>), g, b, 0, st, x, K, xq, xs, xsum);
-    else if (per <= 2) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 2>), g, b, 0, st, x, K, xq, xs, xsum);
-    else if (per <= 4) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 4>), g, b, 0, st, x, K, xq, xs, xsum);
-    else if (per <= 8) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 8>), g, b, 0, st, x, K, xq, xs, xsum);
-    else if (per <= 16) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 16>), g, b, 0, st, x, K, xq, xs, xsum);
+    auto grid = [&](int tpb) { return dim3((unsigned)((N + tpb - 1) / tpb)); };
+    if (pieces <= 64)
+        hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 4>), grid(4), b, 0, st, x, N, K, xq, xs, xsum);
+    else if (pieces <= 128)
+        hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 2>), grid(2), b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 1) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 2) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 2, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 4) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 4, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 8) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 8, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 16) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 16, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
     else hipLaunchKernelGGL(quant_act_kernel<BF16>, g, b, 0, st, x, K, xq, xs, xsum);
     return hipGetLastError();
 }
