@@ -631,14 +631,17 @@ def test_sixteen_token_tiles_ragged(bn, entry):
 
 
 @pytest.mark.parametrize("M,K,N", [(16400, 8192, 16), (16400, 384, 1), (32800, 1024, 11),
-                                   (300, 28672, 13),
-                                   (300, 8192, 16), (33, 128, 5), (4097, 256, 16), (70, 16384, 2)])
+                                   (300, 28672, 13), (1000, 28672, 16), (301, 8320, 9),
+                                   (4111, 12288, 5), (17, 32768, 1),
+                                   (300, 8192, 16), (33, 128, 5), (4097, 256, 16), (70, 16384, 2),
+                                   (2000, 7936, 16)])
 def test_gemm_sixteen_token_mfma(bn, M, K, N):
     """Up to 16 tokens through the prefill entry: 16-token tiles on the
     16x16x64 MFMA -- 128-row or 64-row tiles where a launch has at least 256
     of them, else 32-row tiles with K split over 4 (8 at K >= 16384) wave groups,
-    including fewer K blocks than pipeline stages; M ragged against the
-    tile; sampled rows (all when small) against the oracle."""
+    including fewer K blocks than pipeline stages and block counts the K
+    groups do not divide; M ragged against the tile; sampled rows (all when
+    small) against the oracle."""
     rows = None if M <= 4100 else [(0, 40), (M // 2 + 3, 40), (M - 29, 29)]
     run_case(bn, M, K, N, "gemm", seed=M + K + N, rows=rows)
 
