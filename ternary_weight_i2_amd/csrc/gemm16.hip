@@ -207,8 +207,9 @@ hipError_t launch_gemm16(const GemmMat *mats, int nmats, int64_t K, const int8_t
     // else 32 rows) that still gives every CU a workgroup: 128-row tiles halve
     // the token staging per weight byte (gate/up at K = 8192: 896 workgroups
     // of 64 rows, 448 of 128; 747 -> 740 us per step).
-    int64_t t64r = 0, t128r = 0;
+    int64_t t32r = 0, t64r = 0, t128r = 0;
     for (int i = 0; i < nmats; ++i) {
+        t32r += (mats[i].M + 31) / 32;
         t64r += (mats[i].M + 63) / 64;
         t128r += (mats[i].M + 127) / 128;
     }
@@ -216,8 +217,14 @@ hipError_t launch_gemm16(const GemmMat *mats, int nmats, int64_t K, const int8_t
     if (t64r >= 256) return run_gemm16<64, 2, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     // long reductions (the large layer's down projection, K = 28672): K
     // split over eight wave groups instead of four (877 -> 854 us per step
-    // on the earlier 32-token-wide tiles)
-    if (K >= 16384) return run_gemm16<32, 1, 3, 8>(mats, nmats, K, xq, xs, xsum, N, st);
+    // on the earlier 32-token-wide tiles); so too at K >= 8192 where the
+    // 32-row tiles give each CU at most one workgroup (the large layer's o
+    // projection, 256 tiles: 9.2 -> 7.9 us), so twice the blocks are in flight
+    // per CU.  Not with more tiles than CUs (q/k/v, 320 tiles: 10.2 us on
+    // four groups, 10.4 on eight), and no further gain from more stages
+    // (o: 8.1-8.6 us with five or six).
+    if (K >= 16384 || (K >= 8192 && t32r <= 256))
+        return run_gemm16<32, 1, 3, 8>(mats, nmats, K, xq, xs, xsum, N, st);
     return run_gemm16<32, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
