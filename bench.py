@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "3622edaac634e04d4d232735ac398c88e2ff1393a9cf483f99860abae0c2b809",
+           "sha256": "d85318f87b1aee53c9a04d861280166525a5c01ef3eecd6de75ca7ad43a003d7",
            "bytes_per_launch": 4578304}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 # MFMA busy fraction of the prefill GEMM launches (y only), from rocprofv3

@@ -41,21 +41,28 @@ struct GemvGeometry {
     int lpr;           // lanes per row
     int rows_per_wg;   // rows per workgroup
     int per;           // tokens per pass
-    bool long_rows;    // 16-wave workgroups, one row group per wave
+    bool long_rows;    // 16-wave workgroups, one row per wave in each row group
 };
 // Long rows (a whole wave per row and more than four chunks per lane, i.e.
-// K > 16384) quantised in the kernel (modes 1/2) in a launch of at least 4096
-// rows take 16-wave workgroups of 16 rows: the whole bf16 token then fits the
-// prologue's registers (read once per workgroup instead of twice), and each
-// wave owns one row.  On int8 tokens the 4-wave layout with two row groups
-// per wave is faster (down projection 8192x28672: 14.3 against 15.6 us).
+// K > 16384) in a launch of at least 4096 rows take 16-wave workgroups, each
+// wave one row per row group: the token is staged (int8) or quantised (bf16:
+// the whole row then fits the prologue's registers, read once per workgroup
+// instead of twice) by a quarter as many workgroups as with four waves.  A
+// workgroup takes as many row groups as keep every workgroup resident in
+// one round (the down projection 8192x28672: 256 workgroups of 32 rows;
+// large layer stack at N = 1, int8 tokens 380 -> 365 us per step, fused
+// bf16 455 -> 418 us).
 static GemvGeometry gemv_geometry(int64_t K, int64_t total_rows, int mode) {
     GemvGeometry g;
     const int C = (int)(K >> 6);
     g.lpr = BITNET_GEMV_LPR ? BITNET_GEMV_LPR : pick_lpr(C, total_rows);
-    g.long_rows = mode != 0 && g.lpr == 64 && C > 4 * 64 && total_rows >= 4096;
+    g.long_rows = g.lpr == 64 && C > 4 * 64 && total_rows >= 4096;
     if (g.long_rows) {
-        g.rows_per_wg = kGemvWavesLong;
+        // as many row groups per wave as keep every workgroup resident in one
+        // round (one 16-wave workgroup per CU at this kernel's register count)
+        const int64_t round = (int64_t)kGemvWavesLong * 256;
+        const int64_t iters = (total_rows + round - 1) / round;
+        g.rows_per_wg = (int)(kGemvWavesLong * (iters < 1 ? 1 : iters));
         g.per = (int)(kLdsBytes / K) < 2 ? 1 : 2;
         return g;
     }

@@ -46,7 +46,7 @@
 namespace bitnet {
 
 constexpr int kGemvWaves = 4;        // waves per workgroup (WAVES), short and mid rows
-constexpr int kGemvWavesLong = 16;   // waves per workgroup for long rows (one row group each)
+constexpr int kGemvWavesLong = 16;   // waves per workgroup for long rows (a row per wave per row group)
 constexpr int kLdsBytes = 61440;   // activation staging budget per workgroup (60 KiB)
 #ifndef BITNET_GEMV_TARGET_WGS
 #define BITNET_GEMV_TARGET_WGS 1024   // workgroups per launch before slabs grow

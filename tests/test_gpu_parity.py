@@ -185,8 +185,11 @@ def test_gemv_small(bn, M, K, N):
 
 
 # int8 tokens longer than two 16-byte pieces per thread (staged to LDS before
-# the weights are loaded), one and two tokens, ragged M, K up to 32768
+# the weights are loaded), one and two tokens, ragged M, K up to 32768; from
+# 4096 rows at K > 16384 the 16-wave layout, with one to three row groups per
+# workgroup and a ragged last workgroup
 @pytest.mark.parametrize("M,K,N", [(300, 28672, 1), (300, 28672, 2), (4100, 32768, 1),
+                                   (4100, 28672, 2), (9000, 16512, 1),
                                    (129, 8192, 2), (130, 12288, 1), (70, 9216, 1),
                                    (65, 20480, 2)])
 def test_gemv_long_int8_tokens(bn, M, K, N):
