@@ -195,9 +195,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 // thread issues the loads of all its R 16-byte pieces at once (clamped,
 // always-valid addresses; a repeated last piece cannot change the absmax and
 // is not emitted), so a token costs one memory round trip instead of one per
-// piece and pass.  Short rows (at most 64 or 128 pieces) share a workgroup:
-// TPB tokens, kQuantThreads / TPB threads each, so no thread idles.
-// Identical arithmetic, identical bits.
+// piece and pass.  A workgroup holds TPB tokens of kQuantThreads / TPB
+// threads each (the launcher's choice below).  Identical arithmetic,
+// identical bits.
 template <int BF16, int R, int TPB>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
     const void *__restrict__ x, int64_t N, int64_t K, int8_t *__restrict__ xq,
@@ -275,24 +275,44 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
     }
 }
 
+#ifndef BITNET_QUANT_ROUND
+#define BITNET_QUANT_ROUND 1
+#endif
+
+template <int BF16, int TPB>
+static hipError_t launch_quant_tpb(const void *x, int64_t N, int64_t K, int8_t *xq, float *xs,
+                                   int32_t *xsum, hipStream_t st) {
+    constexpr int T = kQuantThreads / TPB;   // threads per token
+    const int64_t per = (K / Vec16<BF16>::kElems + T - 1) / T;
+    const dim3 g((unsigned)((N + TPB - 1) / TPB)), b(kQuantThreads);
+    if (per <= 1) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, TPB>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 2) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 2, TPB>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 4) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 4, TPB>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else if (per <= 8) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 8, TPB>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    else hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 16, TPB>), g, b, 0, st, x, N, K, xq, xs, xsum);
+    return hipGetLastError();
+}
+
+// Tokens per workgroup: enough that no thread idles on short rows (at most
+// 64 or 128 16-byte pieces: 4 or 2), and at least two once a launch has
+// more tokens than 2048 one-token workgroups (8 per CU) would hold in one
+// resident round; each thread then holds more pieces, all loaded at once.
 template <int BF16>
 static hipError_t launch_quant_t(const void *x, int64_t N, int64_t K, int8_t *xq, float *xs,
                                  int32_t *xsum, hipStream_t st) {
     const int64_t pieces = K / Vec16<BF16>::kElems;
-    const int64_t per = (pieces + kQuantThreads - 1) / kQuantThreads;
-    const dim3 g((unsigned)N), b(kQuantThreads);
-    auto grid = [&](int tpb) { return dim3((unsigned)((N + tpb - 1) / tpb)); };
-    if (pieces <= 64)
-        hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 4>), grid(4), b, 0, st, x, N, K, xq, xs, xsum);
-    else if (pieces <= 128)
-        hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 2>), grid(2), b, 0, st, x, N, K, xq, xs, xsum);
-    else if (per <= 1) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 1, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
-    else if (per <= 2) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 2, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
-    else if (per <= 4) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 4, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
-    else if (per <= 8) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 8, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
-    else if (per <= 16) hipLaunchKernelGGL((quant_act_regs_kernel<BF16, 16, 1>), g, b, 0, st, x, N, K, xq, xs, xsum);
-    else hipLaunchKernelGGL(quant_act_kernel<BF16>, g, b, 0, st, x, K, xq, xs, xsum);
-    return hipGetLastError();
+    int tpb = pieces <= 64 ? 4 : (pieces <= 128 ? 2 : 1);
+    if (BITNET_QUANT_ROUND && N > 2048 && tpb < 2) tpb = 2;
+    // at most 16 pieces per thread in registers; longer rows stream twice
+    while (tpb > 1 && pieces > (int64_t)16 * (kQuantThreads / tpb)) tpb /= 2;
+    if (pieces > (int64_t)16 * kQuantThreads) {
+        hipLaunchKernelGGL(quant_act_kernel<BF16>, dim3((unsigned)N), dim3(kQuantThreads), 0, st, x,
+                           K, xq, xs, xsum);
+        return hipGetLastError();
+    }
+    if (tpb == 4) return launch_quant_tpb<BF16, 4>(x, N, K, xq, xs, xsum, st);
+    if (tpb == 2) return launch_quant_tpb<BF16, 2>(x, N, K, xq, xs, xsum, st);
+    return launch_quant_tpb<BF16, 1>(x, N, K, xq, xs, xsum, st);
 }
 
 hipError_t launch_quant(const void *x, int bf16, int64_t N, int64_t K,

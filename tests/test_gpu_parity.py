@@ -136,7 +136,8 @@ def test_pack_rejects_non_ternary(bn):
 # ------------------------------------------------------------------ quant
 @pytest.mark.parametrize("N,K", [(1, 128), (3, 512), (9, 384), (7, 1024), (1027, 1024),
                                  (17, 2560), (6, 4096), (3, 4224),
-                                 (5, 6912), (2, 8192), (2, 8320), (2, 32768)])
+                                 (5, 6912), (2, 8192), (2, 8320), (2, 32768),
+                                 (2101, 2048), (2049, 3072), (2051, 6912), (2049, 20480)])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_quant_bit_exact(bn, N, K, act):
     rng = np.random.default_rng(N * 7 + K)
