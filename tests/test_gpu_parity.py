@@ -392,11 +392,13 @@ def test_linear_small(bn, Ms, K, N, dtype):
 
 @pytest.mark.parametrize("Ms,K,N,dtype", [((4100,), 28672, 1, "bf16"), ((4100,), 28672, 2, "f32"),
                                           ((2050, 2070), 32768, 2, "bf16"),
-                                          ((4097,), 16512, 1, "bf16"), ((4111,), 28672, 1, "f32")])
+                                          ((4097,), 16512, 1, "bf16"), ((4111,), 28672, 1, "f32"),
+                                          ((8200,), 28672, 1, "bf16"), ((2000, 6300), 20480, 2, "bf16")])
 def test_linear_long_rows(bn, Ms, K, N, dtype):
     """Long rows (K > 16384, a whole wave per row) in launches of at least
-    4096 rows: the fused linear runs 16-wave workgroups of 16 rows, the int8
-    GEMV 4-wave ones; M ragged against both, one and two tokens per pass,
+    4096 rows: 16-wave workgroups, fused and on int8 tokens, each taking as
+    many row groups as keep the launch in one resident round (two or three
+    here); M ragged against the workgroup, one and two tokens per pass,
     every row against the oracle (and fused against unfused bit for bit)."""
     run_linear(bn, list(Ms), K, N, dtype, seed=K + N + sum(Ms))
 
