@@ -43,9 +43,9 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 # profiler's own per-dispatch cost, so those fractions are lower bounds.
 GEMM_COUNTERS = {"sources": ("ternary_weight_i2_amd/csrc/gemm.hip", "ternary_weight_i2_amd/csrc/gemm_tiles.h",
                              "ternary_weight_i2_amd/csrc/common.h"),
-                 "sha256": "0df26041d3a3cc12e52a50651b2c95b58714095241e3370776afcd6648cdeed5",
-                 "mfma_busy": {4096: {"q/k/v": 0.227, "o": 0.149, "gate/up": 0.255, "down": 0.193},
-                               128: {"q/k/v": 0.016, "o": 0.008, "gate/up": 0.023, "down": 0.011}}}
+                 "sha256": "0448e9d019644c6782998acf8491ef7373f5c6e9c238d3d0d6b3de0c5e817ee0",
+                 "mfma_busy": {4096: {"q/k/v": 0.236, "o": 0.153, "gate/up": 0.282, "down": 0.196},
+                               128: {"q/k/v": 0.015, "o": 0.008, "gate/up": 0.023, "down": 0.011}}}
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
 

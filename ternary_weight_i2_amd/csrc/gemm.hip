@@ -43,6 +43,7 @@
 namespace bitnet {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int BM, int BN, int WM, int WN, int kStages, int KS>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const GemmArgs a) {
@@ -233,13 +234,68 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_mfma_kernel(const Gemm
     }
 
     // Result layout (tokens are the MFMA's A operand): lane l, register 4q + j
-    // holds token 8q + 4*(l/32) + j of the fragment and weight row l%32, so
-    // each dword store writes 32 consecutive outputs of two token rows -- two
-    // whole 128-byte segments.  (Weights as the A operand put four rows of one
-    // token in a lane: 16-byte stores, but each instruction touching 32 token
-    // rows 32 bytes at a time; with y and D written that took 188 against
-    // 154 us on the 0.6B-class layer at N = 4096.)  Lane t (t < 32) holds
-    // token t's sum(x) and factor; the others get them by lane shuffle.
+    // holds token 8q + 4*(l/32) + j of the fragment and weight row l%32.
+    // Single-group tiles (the large prefill launches) turn each 32x32
+    // fragment around in LDS (the stages are free once the K loop is done):
+    // the wave writes its raw sums as [token][row] and reads them back as 16
+    // bytes per lane, four rows of one token, so each store instruction
+    // writes eight whole 128-byte token-row segments with a quarter of the
+    // instructions of the per-dword stores below (0.6B-class layer at
+    // N = 4096, y only: 104 -> 96 us).  Lane t (t < 32) holds token t's
+    // sum(x) and factor; the others get them by lane shuffle.
+    if constexpr (KS == 1) {
+        __syncthreads();   // every wave is past its last fragment read of the stages
+        constexpr int LROW = 36;   // ints per staged token row (padded)
+        int *const stg = reinterpret_cast<int *>(lds_all) + wave * 32 * LROW;
+        static_assert(NW * 32 * LROW * 4 <= kStages * STAGE, "epilogue staging fits the stages");
+        const int tl = lane >> 3, rl = 4 * (lane & 7);   // read-back: tokens tl + 8p, rows rl..rl+3
+        const bool vec = (M & 3) == 0;                   // 16-byte aligned output rows
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) {
+            const int nb = n0 + (wn * NJ + nj) * 32;
+            int sx[4];
+            float c[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                sx[p] = __shfl(sxv[nj], tl + 8 * p);
+                c[p] = __shfl(cfac[nj], tl + 8 * p);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int m = m0 + (wm * MI + mi) * 32 + rl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) stg[(8 * q + 4 * kg + j) * LROW + r32] = acc[mi][nj][4 * q + j];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int n = nb + tl + 8 * p;
+                    const v4i r = *reinterpret_cast<const v4i *>(stg + (tl + 8 * p) * LROW + rl);
+                    const v4i d = v4i{r.x - sx[p], r.y - sx[p], r.z - sx[p], r.w - sx[p]};
+                    const int64_t o = (int64_t)n * M + m;
+                    if (vec && n < N && m < M) {   // M % 4 == 0: all four rows exist
+                        if (dot) *reinterpret_cast<v4i *>(dot + o) = d;
+                        if (y) *reinterpret_cast<v4f *>(y + o) =
+                            v4f{(float)d.x * c[p], (float)d.y * c[p], (float)d.z * c[p], (float)d.w * c[p]};
+                    } else if (n < N) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (m + e < M) {
+                                if (dot) dot[o + e] = d[e];
+                                if (y) y[o + e] = (float)d[e] * c[p];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+    // K groups: each dword store writes 32 consecutive outputs of two token
+    // rows -- two whole 128-byte segments.  (Weights as the A operand put four
+    // rows of one token in a lane: 16-byte stores, but each instruction
+    // touching 32 token rows 32 bytes at a time; with y and D written that
+    // took 188 against 154 us on the 0.6B-class layer at N = 4096.)
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
         const int nb = n0 + (wn * NJ + nj) * 32;
