@@ -238,11 +238,25 @@ def time_graph(torch, g, reps, warmup, min_warm_s=0.0):
     return e0.elapsed_time(e1) / 1e3      # seconds
 
 
+def device_clock_mhz():
+    """Peak shader clock the HIP runtime reports for device 0
+    (hipDeviceGetAttribute with hipDeviceAttributeClockRate, entry 5 of the
+    attribute enum, in kHz), or None where the runtime cannot be asked."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    v = ctypes.c_int(0)
+    return v.value / 1000.0 if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0 else None
+
+
 def device_context(torch):
     """The device, and the read rate torch's own sum reaches on 1 GiB of fp32:
     a library read stream for context, not a ceiling (the large-layer GEMV
     row reads faster)."""
     props = torch.cuda.get_device_properties(0)
+    clock_mhz = device_clock_mhz()
     x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     for _ in range(3):
         x.sum()
@@ -259,6 +273,7 @@ def device_context(torch):
     del x
     return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count,
+            "peak_clock_MHz": clock_mhz,
             "torch_sum_read_GBs": round((1 << 30) / t / 1e9, 1),
             "torch_sum_read_method": "torch sum over 1 GiB fp32, 10 reps"}
 
