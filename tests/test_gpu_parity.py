@@ -663,6 +663,17 @@ def test_gemm_mid_tiles_ragged(bn):
     run_case(bn, M, K, N, "gemm", seed=520, rows=[(0, 64), (250, 70), (456, 64)])
 
 
+@pytest.mark.parametrize("M,K,N", [(1027, 256, 4100), (2049, 128, 8200), (1030, 384, 4097)])
+def test_gemm_epilogue_rows_not_multiple_of_four(bn, M, K, N):
+    """Single-group tiles (128x64, and 256x128 where a launch has at least
+    512 of them) write their outputs from an LDS turn-around, 16 bytes per
+    lane where M is a multiple of 4 and element by element otherwise: M and
+    N ragged against the tiles, M not a multiple of 4; sampled rows
+    (including the last, partial row tile) against the oracle."""
+    assert ((M + 127) // 128) * ((N + 127) // 128) >= 256 and M % 4 != 0
+    run_case(bn, M, K, N, "gemm", seed=M + N, rows=[(0, 40), (M // 2 + 1, 37), (M - 29, 29)])
+
+
 @pytest.mark.parametrize("Ms,K,N", [((5, 0, 130), 128, 1), ((640, 640, 2560), 2560, 2),
                                     ((257, 33), 384, 7), ((300, 41, 7), 1280, 24),
                                     ((64, 0, 90), 512, 25), ((100, 200), 640, 64),
