@@ -16,27 +16,41 @@ namespace bitnet {
 // l%16 of the tile, whose 16 bytes for those k are half (l/16)&1 of the row's
 // 32-byte block slice, field 2s + (l/16)/2 -- one 16-byte LDS read per block
 // serves both steps (shift and mask per dword).  The result register i of
-// lane l holds token 4*(l/16) + i for weight row l%16.  Staging (LDS-DMA, one
-// barrier per block), K groups and the epilogue follow gemm_mfma_kernel.
+// lane l holds token 4*(l/16) + i for weight row l%16.
+//
+// Staging: the workgroup's KS K groups share each pipeline stage, which holds
+// KS consecutive blocks (group g computes block g of it): every weight row's
+// KS x 32 bytes and every token's KS x 128 bytes sit contiguously, so each
+// 1 KB LDS-DMA instruction moves 128- or 256-byte runs of a few rows instead
+// of one 32-byte block slice of 32 rows -- a quarter of the requests per
+// byte (large layer at N = 16: 71.6 -> 63.1 us per layer of four launches,
+// N = 7: 64.6 -> 60.5 us).  The 16-byte chunks of a row are XOR-swizzled by
+// row (token) index, so sixteen rows reading the same chunk hit distinct
+// banks.  One barrier per stage; the K groups' sums and the epilogue follow
+// gemm_mfma_kernel.
 template <int BM, int WM, int kStages, int KS>
 __global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArgs a) {
-    static_assert(kStages >= 2 && KS >= 1, "stages, K groups");
-    constexpr int NW = WM;             // waves per K group
-    constexpr int MI = BM / WM / 16;   // 16-row MFMA tiles per wave
+    static_assert(kStages >= 2 && (KS == 4 || KS == 8), "stages, K groups");
+    constexpr int NW = WM;                 // waves per K group
+    constexpr int NWT = WM * KS;           // waves of the workgroup
+    constexpr int MI = BM / WM / 16;       // 16-row MFMA tiles per wave
     static_assert(MI >= 1 && BM % (16 * WM) == 0, "tile shape");
-    constexpr int TA = BM / 32, TB = 2, T = TA + TB;   // 1 KB DMA instructions per block
-    static_assert(BM % 32 == 0, "whole 1 KB DMA instructions");
-    constexpr int CMAX = (T + NW - 1) / NW, CMIN = T / NW;
-    static_assert(CMIN >= 1, "every wave issues at least one DMA per block");
-    constexpr int A_BYTES = BM * kBlockBytes, B_BYTES = 16 * kBlock;
+    constexpr int RB = KS * kBlockBytes;   // weight bytes of one row in a stage
+    constexpr int TBY = KS * kBlock;       // token bytes of one token in a stage
+    constexpr int CPR_A = RB / 16, CPR_B = TBY / 16;   // 16-byte chunks per row
+    constexpr int A_BYTES = BM * RB, B_BYTES = 16 * TBY;
     constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int TA = A_BYTES / 1024, TB = B_BYTES / 1024, T = TA + TB;
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "whole 1 KB DMA instructions");
+    constexpr int RPI = 1024 / RB, TPI = 1024 / TBY;   // weight rows / tokens per instruction
+    constexpr int CMAX = (T + NWT - 1) / NWT, CMIN = T / NWT;
+    static_assert(CMIN >= 1, "every wave issues at least one DMA per stage");
     constexpr int RED = KS > 1 ? (KS - 1) * NW * MI * 4 * 64 * 4 : 0;
-    static_assert(RED <= KS * kStages * STAGE, "partial sums reuse the staging memory");
-    __shared__ __attribute__((aligned(1024))) int8_t lds_all[KS * kStages * STAGE];
+    static_assert(RED <= kStages * STAGE, "partial sums reuse the staging memory");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = (tid >> 6) % NW, grp = (tid >> 6) / NW;
-    int8_t *const lds = lds_all + grp * (kStages * STAGE);
+    const int lane = tid & 63, wt = tid >> 6, wave = wt % NW, grp = wt / NW;
     const int c16 = lane & 15, g4 = lane >> 4;
     const int total = (int)gridDim.x;
     int id = (int)blockIdx.x;
@@ -58,33 +72,47 @@ __global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArg
     const int m0 = (local % mtiles) * BM, n0 = (local / mtiles) * 16;
     const int64_t rowb = K >> 2;
     const int nkb = K / kBlock;
-    const int nit = (nkb + KS - 1) / KS;
+    const int nit = (nkb + KS - 1) / KS;   // stages of KS blocks (group g computes block g)
 
-    // DMA sources, as gemm_mfma_kernel (rows and tokens past the end clamped)
-    const bool full = wave < T - CMIN * NW;
+    // slot swizzles: sixteen consecutive weight rows (tokens) reading the same
+    // chunk land on distinct banks
+    auto swz_a = [](int r) { return KS == 4 ? (r >> 1) & 7 : r & 15; };
+    auto swz_b = [](int t) { return t & 15; };
+
+    // DMA instructions of a stage (weight rows first, then tokens) are dealt
+    // to all waves round-robin; this lane's source of each: its row (token),
+    // its chunk's block within the stage (clamped to the last block of K at
+    // the tail) and the chunk's offset in that block.  Rows and tokens past
+    // the matrix are clamped (their results are never stored).
+    const bool full = wt < T - CMIN * NWT;
     const int8_t *src[CMAX];
-    int64_t step[CMAX];
+    int cb[CMAX], bstep[CMAX];
 #pragma unroll
     for (int c = 0; c < CMAX; ++c) {
-        const int j = min(wave + NW * c, T - 1);
+        const int j = min(wt + NWT * c, T - 1);
         if (j < TA) {
-            const int row = 32 * j + (lane >> 1);
+            const int row = j * RPI + lane / CPR_A;
+            const int chunk = (lane % CPR_A) ^ swz_a(row);
+            cb[c] = chunk >> 1;
+            bstep[c] = kBlockBytes;
             src[c] = reinterpret_cast<const int8_t *>(packed) +
-                     (int64_t)min(m0 + row, M - 1) * rowb + 16 * (lane & 1);
-            step[c] = kBlockBytes;
+                     (int64_t)min(m0 + row, M - 1) * rowb + 16 * (chunk & 1);
         } else {
-            const int row = 8 * (j - TA) + (lane >> 3);
-            const int piece = (lane & 7) ^ tok_swz(row);
-            src[c] = xq + (int64_t)min(n0 + row, N - 1) * K + 16 * piece;
-            step[c] = kBlock;
+            const int t = (j - TA) * TPI + lane / CPR_B;
+            const int chunk = (lane % CPR_B) ^ swz_b(t);
+            cb[c] = chunk >> 3;
+            bstep[c] = kBlock;
+            src[c] = xq + (int64_t)min(n0 + t, N - 1) * K + 16 * (chunk & 7);
         }
     }
-    auto issue = [&](int kb, int st) {
+    auto issue = [&](int it2, int st) {
+        const int kb0 = min(it2, nit - 1) * KS;
         const int8_t *base = lds + st * STAGE;
 #pragma unroll
         for (int c = 0; c < CMAX; ++c)
             if (c < CMIN || full)
-                dma16(src[c] + (int64_t)kb * step[c], lds_addr_of(base + 1024 * (wave + NW * c)));
+                dma16(src[c] + (int64_t)min(kb0 + cb[c], nkb - 1) * bstep[c],
+                      lds_addr_of(base + 1024 * (wt + NWT * c)));
     };
     auto wait_block = [&]() {
         if (full) wait_vmcnt<CMAX * (kStages - 2)>();
@@ -103,26 +131,30 @@ __global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArg
     v4i acc[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) acc[mi] = v4i{0, 0, 0, 0};
-    const int tsw = tok_swz(c16);
     const int sh0 = 6 - 2 * (g4 >> 1);   // field 2s + g4/2 sits at bit 6 - 2*field
 
+    // kStages-1 stages in flight (past the end the last stage is fetched
+    // again into a stage that is never read), so the wait is a constant
 #pragma unroll
-    for (int p = 0; p < kStages - 1; ++p) issue(min(p * KS + grp, nkb - 1), p);
+    for (int p = 0; p < kStages - 1; ++p) issue(p, p);
     for (int it = 0; it < nit; ++it) {
         wait_block();
-        __syncthreads();
-        issue(min((it + kStages - 1) * KS + grp, nkb - 1), (it + kStages - 1) % kStages);
-        if (KS > 1 && it * KS + grp >= nkb) continue;
+        __syncthreads();   // the stage is in LDS; stage (it-1) is free for the next DMA
+        issue(it + kStages - 1, (it + kStages - 1) % kStages);
+        if (it * KS + grp >= nkb) continue;   // past the end of K for this group
         const int8_t *sa = lds + (it % kStages) * STAGE;
         const int8_t *sb = sa + A_BYTES;
         v4i wf[MI], tf[2];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            wf[mi] = *reinterpret_cast<const v4i *>(sa + ((wave * MI + mi) * 16 + c16) * kBlockBytes +
-                                                    16 * (g4 & 1));
+        for (int mi = 0; mi < MI; ++mi) {
+            const int row = (wave * MI + mi) * 16 + c16;
+            wf[mi] = *reinterpret_cast<const v4i *>(sa + row * RB +
+                                                    16 * ((2 * grp + (g4 & 1)) ^ swz_a(row)));
+        }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-            tf[s2] = *reinterpret_cast<const v4i *>(sb + c16 * kBlock + 16 * ((4 * s2 + g4) ^ tsw));
+            tf[s2] = *reinterpret_cast<const v4i *>(sb + c16 * TBY +
+                                                    16 * ((8 * grp + 4 * s2 + g4) ^ swz_b(c16)));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int sh = sh0 - 4 * s2;
@@ -137,7 +169,7 @@ __global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArg
     wait_vmcnt<0>();   // drain the trailing re-fetches before the workgroup ends
     if constexpr (KS > 1) {
         __syncthreads();
-        int *red = reinterpret_cast<int *>(lds_all);
+        int *red = reinterpret_cast<int *>(lds);
         if (grp > 0) {
             int *dst = red + (((grp - 1) * NW + wave) * MI * 4) * 64 + lane;
 #pragma unroll
@@ -155,9 +187,9 @@ __global__ __launch_bounds__(WM * KS * 64) void gemm16_mfma_kernel(const GemmArg
                 for (int e = 0; e < 4; ++e) acc[mi][e] += srcp[(mi * 4 + e) * 64];
         }
     }
+#pragma unroll
     // lane l: weight row m = tile row + l%16, tokens 4*(l/16) + i; consecutive
     // lanes write consecutive outputs of a token row
-#pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         const int m = m0 + (wave * MI + mi) * 16 + c16;
 #pragma unroll
@@ -206,14 +238,17 @@ hipError_t launch_gemm16(const GemmMat *mats, int nmats, int64_t K, const int8_t
     // discarded, 747 on the 16x16x64 MFMA).  The tallest row tile (128, 64,
     // else 32 rows) that still gives every CU a workgroup: 128-row tiles halve
     // the token staging per weight byte (gate/up at K = 8192: 896 workgroups
-    // of 64 rows, 448 of 128; 747 -> 740 us per step).
+    // of 64 rows, 448 of 128; 747 -> 740 us per step).  With the shared
+    // stages, 128-row tiles take two stages (48 KB, so a CU holds up to three
+    // workgroups) and 32-row tiles four (large layer, four launches at N = 16:
+    // 63.3 -> 61.4-62.5 us; N = 7: 60.5 -> 57.3-57.7 us).
     int64_t t32r = 0, t64r = 0, t128r = 0;
     for (int i = 0; i < nmats; ++i) {
         t32r += (mats[i].M + 31) / 32;
         t64r += (mats[i].M + 63) / 64;
         t128r += (mats[i].M + 127) / 128;
     }
-    if (t128r >= 256) return run_gemm16<128, 2, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+    if (t128r >= 256) return run_gemm16<128, 2, 2, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     if (t64r >= 256) return run_gemm16<64, 2, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
     // long reductions (the large layer's down projection, K = 28672): K
     // split over eight wave groups instead of four (877 -> 854 us per step
@@ -221,11 +256,10 @@ hipError_t launch_gemm16(const GemmMat *mats, int nmats, int64_t K, const int8_t
     // 32-row tiles give each CU at most one workgroup (the large layer's o
     // projection, 256 tiles: 9.2 -> 7.9 us), so twice the blocks are in flight
     // per CU.  Not with more tiles than CUs (q/k/v, 320 tiles: 10.2 us on
-    // four groups, 10.4 on eight), and no further gain from more stages
-    // (o: 8.1-8.6 us with five or six).
+    // four groups, 10.4 on eight).
     if (K >= 16384 || (K >= 8192 && t32r <= 256))
-        return run_gemm16<32, 1, 3, 8>(mats, nmats, K, xq, xs, xsum, N, st);
-    return run_gemm16<32, 1, 3, 4>(mats, nmats, K, xq, xs, xsum, N, st);
+        return run_gemm16<32, 1, 4, 8>(mats, nmats, K, xq, xs, xsum, N, st);
+    return run_gemm16<32, 1, 4, 4>(mats, nmats, K, xq, xs, xsum, N, st);
 }
 
 }  // namespace bitnet
