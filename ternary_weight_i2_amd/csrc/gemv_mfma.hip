@@ -18,16 +18,16 @@
 // no second pass and no global scratch is needed; the epilogue then writes
 // D = R - sum(x) and y = D * alpha / s.
 //
-// Operand layout: the B operand (tokens) is read in its natural row-major
-// order straight from global memory (the int8 tokens are small and stay in
-// L2): for MFMA step s (64 k) lane (j, kq) holds x[j][64s + 16kq .. +15].  The
-// contraction is order-free, so the A operand is built to match: those 16
-// positions are one 2-bit field of the 16 packed bytes of half kq%2 of block
-// s/2 (field 2*(s%2) + kq/2).  A lane loads its 16-byte half-block once per
-// block (lanes kq and kq^2 load the same bytes in the same instruction, which
-// the memory pipeline merges) and extracts the two fields it needs with one
-// shift and one mask per dword.  Each wave double-buffers its blocks: the
-// next block's A and B loads are in flight while the current one is used.
+// Operand layout: K advances a pair of 128-weight blocks at a time.  Lane
+// (j, kq) loads the 16-byte half kq%2 of block kq/2 of the pair for weight
+// row j, so the four lanes of a row read the pair's 64 contiguous packed
+// bytes in one instruction, and MFMA step s (s = 0..3) takes the 2-bit field
+// s of those bytes: positions 128*(kq/2) + 32s + 16*(kq%2) + 0..15 of the
+// pair (the contraction is order-free).  The B operand (tokens) is built to
+// match: the same 16 positions of token j, one 16-byte load straight from
+// global memory (the int8 tokens are small and stay in L2).  One shift and
+// one mask per dword extract a field.  Each wave double-buffers its pairs:
+// the next pair's A and B loads are in flight while the current one is used.
 #include "common.h"
 
 namespace bitnet {
@@ -76,10 +76,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
         sse[e] = xs[nn];
     }
 
+    // K advances two 128-weight blocks (a pair) at a time, the waves taking
+    // contiguous ranges of pairs
     const int nblk = K >> 7;
-    const int b0 = (int)((int64_t)nblk * wv / WAVES);
-    const int b1 = (int)((int64_t)nblk * (wv + 1) / WAVES);
+    const int npair = (nblk + 1) >> 1;
+    const int p0 = (int)((int64_t)npair * wv / WAVES);
+    const int p1 = (int)((int64_t)npair * (wv + 1) / WAVES);
     const int64_t rowb = K >> 2;
+    const int hb = kq >> 1;   // this lane's block of the pair
 
     const uint8_t *prow[MI];
 #pragma unroll
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
         const int n = nj * 16 + li;
-        xrow[nj] = xq + (int64_t)(n < N ? n : 0) * K + kq * 16;
+        xrow[nj] = xq + (int64_t)(n < N ? n : 0) * K + (kq & 1) * 16;
     }
 
     v4i acc[MI][NJ];
@@ -100,46 +104,53 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_mfma_kernel(const GemmArgs a)
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = v4i{0, 0, 0, 0};
 
-    // Rows past M and tokens past N load row 0 / token 0 (valid addresses)
-    // and are not zeroed: a row or token only feeds its own output row or
-    // column, which is never stored.  Loading without a select lets the
-    // compiler wait for a block only where its MFMAs use it.
-    auto load = [&](int b, v4i *A, v4i (*B)[NJ]) {
+    // Lane (j, kq) loads the 16-byte half kq%2 of block 2p + kq/2 of its row
+    // -- the four lanes of a row read its pair's 64 contiguous bytes, one
+    // request per two blocks instead of a 32-byte slice per block read twice
+    // -- and its MFMA step s (64 k) takes field s of those bytes, i.e. the
+    // 16 positions 128*(2p + kq/2) + 32s + 16*(kq%2) + 0..15; the token
+    // operand is those 16 bytes of token j, read straight from L2.  Rows past
+    // M and tokens past N load row 0 / token 0 (valid addresses) and are not
+    // zeroed: a row or token only feeds its own output row or column, which is
+    // never stored.  The second block of an odd tail pair is clamped to the
+    // last block and its codes masked to 0.
+    auto load = [&](int p, v4i *A, v4i (*B)[NJ]) {
+        const int64_t b = min(2 * p + hb, nblk - 1);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-            A[mi] = __builtin_nontemporal_load(
-                reinterpret_cast<const v4i *>(prow[mi] + (int64_t)b * 32));
+            A[mi] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(prow[mi] + b * 32));
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj)
-                B[s2][nj] = *reinterpret_cast<const v4i *>(xrow[nj] + (int64_t)b * 128 + s2 * 64);
+                B[s][nj] = *reinterpret_cast<const v4i *>(xrow[nj] + b * 128 + s * 32);
     };
-    auto compute = [&](const v4i *A, v4i (*B)[NJ]) {
+    auto compute = [&](int p, const v4i *A, v4i (*B)[NJ]) {
+        const int msk = 2 * p + hb < nblk ? 0x03030303 : 0;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int sh = 6 - 2 * (2 * s2 + (kq >> 1));
+        for (int s = 0; s < 4; ++s) {
+            const int sh = 6 - 2 * s;
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const v4i a = v4i{(A[mi].x >> sh) & 0x03030303, (A[mi].y >> sh) & 0x03030303,
-                                  (A[mi].z >> sh) & 0x03030303, (A[mi].w >> sh) & 0x03030303};
+                const v4i a = v4i{(A[mi].x >> sh) & msk, (A[mi].y >> sh) & msk,
+                                  (A[mi].z >> sh) & msk, (A[mi].w >> sh) & msk};
 #pragma unroll
                 for (int nj = 0; nj < NJ; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, B[s2][nj], acc[mi][nj],
+                    acc[mi][nj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, B[s][nj], acc[mi][nj],
                                                                         0, 0, 0);
             }
         }
     };
 
     v4i A0[MI], A1[MI];
-    v4i B0[2][NJ], B1[2][NJ];
-    if (b0 < b1) load(b0, A0, B0);
-    for (int b = b0; b < b1; b += 2) {
-        if (b + 1 < b1) load(b + 1, A1, B1);
-        compute(A0, B0);
-        if (b + 1 >= b1) break;
-        if (b + 2 < b1) load(b + 2, A0, B0);
-        compute(A1, B1);
+    v4i B0[4][NJ], B1[4][NJ];
+    if (p0 < p1) load(p0, A0, B0);
+    for (int p = p0; p < p1; p += 2) {
+        if (p + 1 < p1) load(p + 1, A1, B1);
+        compute(p, A0, B0);
+        if (p + 1 >= p1) break;
+        if (p + 2 < p1) load(p + 2, A0, B0);
+        compute(p + 1, A1, B1);
     }
 
     __syncthreads();   // acc_lds zeroed by every thread before any add
