@@ -12,7 +12,7 @@
 //
 // Work split: a workgroup owns BM = 16*MI rows of one matrix and all N
 // tokens (NJ 16-token tiles) over the full K, which its WAVES waves split
-// into contiguous block ranges.  One launch serves up to kMaxMats matrices
+// into contiguous ranges of block pairs.  One launch serves up to kMaxMats matrices
 // that share K and the tokens (q/k/v, gate/up): workgroups
 // [tile_begin, next tile_begin) belong to matrix i.  Partial sums meet in LDS through exact integer adds (ds_add), so
 // no second pass and no global scratch is needed; the epilogue then writes
