@@ -216,10 +216,11 @@ static hipError_t run_w(int waves, const GemmMat *mats, int nmats, int64_t K, co
 template <int NJ>
 static hipError_t run_nj(const GemmMat *mats, int nmats, int64_t K, const int8_t *xq,
                          const float *xs, const int32_t *xsum, int64_t N, hipStream_t st) {
-    // waves split K: about two or more 128-weight blocks per wave.  17..20
-    // blocks (K = 2560) take ten waves, at most two blocks each, so no wave
-    // needs a third round trip to memory while the others wait for it at the
-    // reduction (2-3% less time per 2B-class step than eight waves).
+    // waves split K: about one or more pairs of 128-weight blocks per wave.
+    // 17..20 blocks (K = 2560) take ten waves, at most one pair each, so no
+    // wave needs a second round trip to memory while the others wait for it
+    // at the reduction (measured with one block per step: 2-3% less time per
+    // 2B-class step than eight waves).
     const int64_t nblk = K / 128;
     const int waves = nblk >= 32 ? 16 : (nblk > 16 && nblk <= 20) ? 10 : (nblk >= 16 ? 8 : 4);
     // rows per workgroup: 16 (most workgroups in flight at once), or 32 --
