@@ -177,7 +177,8 @@ def test_quant_edge_rows(bn):
 SMALL = [(1, 128, 1), (5, 128, 2), (17, 384, 3), (64, 256, 4), (100, 640, 5),
          (129, 1152, 8), (33, 512, 9), (70, 896, 16), (40, 2176, 5), (33, 8192, 3),
          (50, 640, 17), (50, 640, 24),
-         (130, 256, 31), (31, 384, 32), (60, 384, 33), (97, 1280, 40), (65, 384, 64)]
+         (130, 256, 31), (31, 384, 32), (60, 384, 33), (97, 1280, 40), (65, 384, 64),
+         (40, 128, 7), (21, 640, 12)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL)
