@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "d85318f87b1aee53c9a04d861280166525a5c01ef3eecd6de75ca7ad43a003d7",
-           "bytes_per_launch": 4578304}
+           "sha256": "1b9482d7b7edd51546c31559d4165ce652c4d42e5f242e0167d79c295e9473a3",
+           "bytes_per_launch": 4574720}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 # MFMA busy fraction of the prefill GEMM launches (y only), from rocprofv3
 # SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs)
