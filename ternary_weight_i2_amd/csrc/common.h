@@ -103,10 +103,26 @@ __device__ __forceinline__ float quant_scale(float amax) {
     const float denom = amax > 1e-5f ? amax : 1e-5f;
     return (float)(127.0 / (double)denom);
 }
-__device__ __forceinline__ int quant_one(float v, float s) {
-    float r = __builtin_rintf(v * s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
+// quant_bits gives q in the low byte of its result: the product is clamped to
+// [-128, 127] before it is rounded (the same result: rounding cannot cross
+// either bound), and adding 1.5 * 2^23 rounds it to an integer, half to even,
+// leaving that integer in the low mantissa bits -- the low byte is its two's
+// complement int8.  Three VALU operations, with no conversion to int and no
+// shifts for packing.
+__device__ __forceinline__ uint32_t quant_bits(float v, float s) {
+    const float t = fminf(fmaxf(v * s, -128.0f), 127.0f);
+    return __float_as_uint(t + 12582912.0f);
+}
+// Low bytes of four words -> one word (b0 in byte 0): three v_perm_b32.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);   // b0.0 b1.0 0 0
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);   // b2.0 b3.0 0 0
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+// Sum of the four int8 codes of a packed word, added to acc.
+__device__ __forceinline__ int sum_codes4(uint32_t packed, int acc) {
+    return __builtin_amdgcn_sdot4((int)packed, 0x01010101, acc, false);
 }
 
 // Grouped decode launch: up to kMaxMats matrices that share K and the same

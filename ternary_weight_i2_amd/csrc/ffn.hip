@@ -315,11 +315,10 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
     uint32_t *q4 = reinterpret_cast<uint32_t *>(xq + row);
     for (int q = tid; q < nq; q += kFfnThreads) {
         const float4 v = hl[q];
-        const int c0 = quant_one(v.x, s), c1 = quant_one(v.y, s), c2 = quant_one(v.z, s),
-                  c3 = quant_one(v.w, s);
-        sum += c0 + c1 + c2 + c3;
-        q4[q] = (uint32_t)(uint8_t)c0 | (uint32_t)(uint8_t)c1 << 8 |
-                (uint32_t)(uint8_t)c2 << 16 | (uint32_t)(uint8_t)c3 << 24;
+        const uint32_t c = pack_low_bytes(quant_bits(v.x, s), quant_bits(v.y, s),
+                                          quant_bits(v.z, s), quant_bits(v.w, s));
+        sum = sum_codes4(c, sum);
+        q4[q] = c;
     }
     sum = wave_sum_i32(sum);
     if (lane == 0) sh.redi[wv] = sum;

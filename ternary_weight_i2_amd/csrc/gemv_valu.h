@@ -90,8 +90,9 @@ __device__ __forceinline__ int lds_pos(int t, int K, int k) {
     return t * K + i * (K >> 2) + 32 * b + 16 * h + e;
 }
 
-// Quantise ntok tokens of x (fp32 or bf16) into LDS; per-token s and sum
-// land in s_tok / sum_tok.  Workgroup 0 also writes the optional outputs.
+// Quantise ntok tokens of x (fp32 or bf16) into LDS; per-token s lands in
+// s_tok and each wave's part of the per-token sum in redi (token_sums adds
+// them after the barrier).  Workgroup 0 also writes the optional outputs.
 // Short tokens (at most XR 16-byte pieces per thread) take the register path:
 // load_tokens() issues every piece load up front -- before the caller issues
 // its weight loads, so waiting for the tokens never waits for the weights --
@@ -123,7 +124,7 @@ struct TokenPrologue {
         }
     }
     __device__ void finish(const GemvArgs &a, bool in_regs, int8_t *xl, float *s_tok,
-                           int *sum_tok, float (*redf)[NT], int (*redi)[NT]) {
+                           float (*redf)[NT], int (*redi)[NT]) {
         const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
         const int K = a.K, nq = K / E;
         const char *x = reinterpret_cast<const char *>(a.x);
@@ -171,12 +172,11 @@ struct TokenPrologue {
         auto emit = [&](int t, int q, const float *v) {
             uint32_t pq[E / 4];
 #pragma unroll
-            for (int j = 0; j < E / 4; ++j) pq[j] = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int qi = quant_one(v[e], s[t]);
-                sm[t] += qi;
-                pq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+            for (int j = 0; j < E / 4; ++j) {
+                pq[j] = pack_low_bytes(quant_bits(v[4 * j], s[t]), quant_bits(v[4 * j + 1], s[t]),
+                                       quant_bits(v[4 * j + 2], s[t]),
+                                       quant_bits(v[4 * j + 3], s[t]));
+                sm[t] = sum_codes4(pq[j], sm[t]);
             }
             const int pos = lds_pos(t, K, q * E);
             if constexpr (E == 8) {
@@ -209,21 +209,28 @@ struct TokenPrologue {
             }
             sm[t] = wave_sum_i32(sm[t]);
         }
+        // The waves' partial sums are combined after the caller's barrier
+        // (token_sums), so no barrier of its own stands before the dot products.
         if (lane == 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) redi[wv][t] = sm[t];
         }
-        __syncthreads();
         if (tid < NT && tid < a.ntok) {
-            int total = 0;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) total += redi[w][tid];
             s_tok[tid] = s[tid];
-            sum_tok[tid] = total;
-            if (blockIdx.x == 0) {
-                if (a.xs_out) a.xs_out[tid] = s[tid];
-                if (a.xsum_out) a.xsum_out[tid] = total;
-            }
+            if (blockIdx.x == 0 && a.xs_out) a.xs_out[tid] = s[tid];
+        }
+    }
+    // After the barrier that follows finish(): every thread's copy of the
+    // per-token sums; workgroup 0 also writes the optional output.
+    __device__ static void token_sums(const GemvArgs &a, const int (*redi)[NT], int *tsum) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            int v = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) v += redi[w][t];
+            tsum[t] = v;
+            if (blockIdx.x == 0 && threadIdx.x == t && t < a.ntok && a.xsum_out)
+                a.xsum_out[t] = v;
         }
     }
 };
@@ -362,9 +369,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelA
         __builtin_amdgcn_sched_barrier(0);       // keep the token loads ahead of the weights
         load_group(0, cur);
         __builtin_amdgcn_sched_barrier(0);
-        tp.finish(a, in_regs, xl, s_tok, sum_tok, redf, redi);
+        tp.finish(a, in_regs, xl, s_tok, redf, redi);
     }
     __syncthreads();
+    int tsum[NT];   // per-token sums of the quantised tokens
+    if constexpr (MODE == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tsum[t] = sum_tok[t];
+    } else {
+        TokenPrologue<NT, MODE, WAVES>::token_sums(a, redi, tsum);
+    }
 
     const int gstride = K >> 2;   // bytes between fields in LDS
     int32_t *dot = a.mat[mi].dot;
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelA
                 // a4 and a16 are exact multiples of 4 and 16
                 const int r = group_sum_i32<LPR>(a1[t] + (a4[t] >> 2) + (a16[t] >> 4));
                 if (u == t && row_ok) {
-                    const int d = r - sum_tok[t];
+                    const int d = r - tsum[t];
                     if (dot) dot[(int64_t)t * M + row] = d;
                     if (y) y[(int64_t)t * M + row] = ((float)d * alpha) / s_tok[t];
                 }

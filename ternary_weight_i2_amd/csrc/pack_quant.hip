@@ -166,12 +166,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
         V::load(row, i, v);
         uint32_t packedq[E / 4];
 #pragma unroll
-        for (int j = 0; j < E / 4; ++j) packedq[j] = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int qi = quant_one(v[e], s);
-            sum += qi;
-            packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+        for (int j = 0; j < E / 4; ++j) {
+            packedq[j] = pack_low_bytes(quant_bits(v[4 * j], s), quant_bits(v[4 * j + 1], s),
+                                        quant_bits(v[4 * j + 2], s), quant_bits(v[4 * j + 3], s));
+            sum = sum_codes4(packedq[j], sum);
         }
         if (E == 8) {
             reinterpret_cast<uint2 *>(qrow)[i] = make_uint2(packedq[0], packedq[E / 4 - 1]);
@@ -247,12 +245,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_regs_kernel(
             V::widen(raw[r], v);
             uint32_t packedq[E / 4];
 #pragma unroll
-            for (int j = 0; j < E / 4; ++j) packedq[j] = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int qi = quant_one(v[e], s);
-                sum += qi;
-                packedq[e / 4] |= ((uint32_t)qi & 0xffu) << (8 * (e % 4));
+            for (int j = 0; j < E / 4; ++j) {
+                packedq[j] = pack_low_bytes(quant_bits(v[4 * j], s), quant_bits(v[4 * j + 1], s),
+                                            quant_bits(v[4 * j + 2], s), quant_bits(v[4 * j + 3], s));
+                sum = sum_codes4(packedq[j], sum);
             }
             if (valid) {
                 if (E == 8) {
