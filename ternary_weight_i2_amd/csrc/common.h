@@ -20,14 +20,17 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// Cross-lane moves inside a row of 16 lanes through DPP (no LDS round trip).
-// Controls: quad_perm [1,0,3,2] and [2,3,0,1] swap neighbours at distance 1
-// and 2; row_half_mirror reads lane 7-i of each 8-lane half row; row_mirror
-// reads lane 15-i of the row.
+// Cross-lane moves through DPP (no LDS round trip).  Inside a row of 16
+// lanes: quad_perm [1,0,3,2] and [2,3,0,1] swap neighbours at distance 1 and
+// 2; row_half_mirror reads lane 7-i of each 8-lane half row; row_mirror reads
+// lane 15-i of the row.  Across rows (gfx9 DPP): row_bcast:15 hands lane 15 of
+// each row to the next row, row_bcast:31 hands lane 31 to rows 2 and 3.
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
@@ -36,11 +39,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
 }
+// A cross-row move into the rows of ROWMASK only; the other rows receive 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_rows_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
 
-// Sum over each aligned group of L lanes (L = 8, 16, 32 or 64); every lane of
-// the group receives the sum.  Once neighbours at distance 1 and 2 are added
-// every lane holds its quad's sum, so mirroring within 8 and then 16 lanes
-// pairs whole quads and then whole halves; the two cross-row steps shuffle.
+// Sum over each aligned group of L lanes (L = 8, 16, 32 or 64).  Once
+// neighbours at distance 1 and 2 are added every lane holds its quad's sum,
+// so mirroring within 8 and then 16 lanes pairs whole quads and then whole
+// halves: for L <= 16 every lane of the group receives the sum.  Groups of 32
+// and 64 lanes then add whole rows with row_bcast: the sum is complete in the
+// group's last row of 16 lanes only (lanes 16..31 of a 32-lane group, 48..63
+// of the wave).
 template <int L>
 __device__ __forceinline__ int group_sum_i32(int v) {
     static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group of 8..64 lanes");
@@ -48,20 +59,53 @@ __device__ __forceinline__ int group_sum_i32(int v) {
     v += dpp_i32<kDppXor2>(v);
     v += dpp_i32<kDppHalfMirror>(v);
     if constexpr (L >= 16) v += dpp_i32<kDppMirror>(v);
-    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (L >= 32) v += dpp_rows_i32<kDppRowBcast15, 0xA>(v);   // rows 1, 3 += rows 0, 2
+    if constexpr (L >= 64) v += dpp_rows_i32<kDppRowBcast31, 0xC>(v);   // rows 2, 3 += rows 0-1
     return v;
 }
-__device__ __forceinline__ int wave_sum_i32(int v) { return group_sum_i32<64>(v); }
-// Wave-wide maximum (fmaxf ignores a NaN operand, so the order is immaterial).
+// Wave-wide sum, returned to every lane (read from lane 63).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    return __builtin_amdgcn_readlane(group_sum_i32<64>(v), 63);
+}
+// Wave-wide maximum of non-negative values, returned to every lane (fmaxf
+// ignores a NaN operand; the rows a cross-row move skips receive 0, which
+// cannot raise the maximum).
 __device__ __forceinline__ float wave_max_f32(float v) {
     v = fmaxf(v, dpp_f32<kDppXor1>(v));
     v = fmaxf(v, dpp_f32<kDppXor2>(v));
     v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
     v = fmaxf(v, dpp_f32<kDppMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    v = fmaxf(v, __int_as_float(dpp_rows_i32<kDppRowBcast15, 0xA>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_rows_i32<kDppRowBcast31, 0xC>(__float_as_int(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// 64-bit lane moves (two 32-bit DPP moves) and the wave-wide sum of 64-bit
+// integers, returned to every lane (read from lane 63).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
+    return (uint64_t)hi << 32 | lo;
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_rows_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp_rows_i32<CTRL, ROWMASK>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp_rows_i32<CTRL, ROWMASK>((int)(uint32_t)(v >> 32));
+    return (uint64_t)hi << 32 | lo;
+}
+__device__ __forceinline__ uint64_t readlane63_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return (uint64_t)hi << 32 | lo;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+    v += dpp_u64<kDppXor1>(v);
+    v += dpp_u64<kDppXor2>(v);
+    v += dpp_u64<kDppHalfMirror>(v);
+    v += dpp_u64<kDppMirror>(v);
+    v += dpp_rows_u64<kDppRowBcast15, 0xA>(v);
+    v += dpp_rows_u64<kDppRowBcast31, 0xC>(v);
+    return readlane63_u64(v);
 }
 
 // s_waitcnt immediate that waits until at most `v` vector-memory operations of
@@ -103,14 +147,16 @@ __device__ __forceinline__ float quant_scale(float amax) {
     const float denom = amax > 1e-5f ? amax : 1e-5f;
     return (float)(127.0 / (double)denom);
 }
-// quant_bits gives q in the low byte of its result: the product is clamped to
-// [-128, 127] before it is rounded (the same result: rounding cannot cross
-// either bound), and adding 1.5 * 2^23 rounds it to an integer, half to even,
-// leaving that integer in the low mantissa bits -- the low byte is its two's
-// complement int8.  Three VALU operations, with no conversion to int and no
-// shifts for packing.
+// quant_bits gives q in the low byte of its result: adding 1.5 * 2^23 to the
+// fp32 product rounds it to an integer, half to even, and leaves that integer
+// in the low mantissa bits -- the low byte is its two's complement int8.  No
+// clamp is needed for finite tokens: |x| <= max(amax, 1e-5) and s is that
+// bound's 127 / d rounded, so |x * s| <= 127 (1 + 2^-24)^2 < 127.5 rounds to
+// at most 127 in magnitude.  Two VALU operations, with no conversion to int
+// and no shifts for packing.
 __device__ __forceinline__ uint32_t quant_bits(float v, float s) {
-    const float t = fminf(fmaxf(v * s, -128.0f), 127.0f);
+#pragma clang fp contract(off)
+    const float t = v * s;   // rounded on its own: never fused with the add
     return __float_as_uint(t + 12582912.0f);
 }
 // Low bytes of four words -> one word (b0 in byte 0): three v_perm_b32.

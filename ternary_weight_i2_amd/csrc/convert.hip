@@ -37,12 +37,6 @@ __device__ __forceinline__ void load4(const void *w, int64_t g, float *v) {
     }
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64c(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 // Pass 1: the digits of sum |w| over groups of 4 weights g = b*256 + t,
 // g += gridDim*256, normalised into partial[b][0..kMagNorm).
 //
@@ -116,7 +110,7 @@ __global__ __launch_bounds__(kConvThreads) void absmean_partial_kernel(
         abs_fold(bk, tid, d);
     }
 #pragma unroll
-    for (int i = 0; i < kMagDigits; ++i) d[i] = wave_sum_u64c(d[i]);
+    for (int i = 0; i < kMagDigits; ++i) d[i] = wave_sum_u64(d[i]);
     if ((tid & 63) == 0) {
 #pragma unroll
         for (int i = 0; i < kMagDigits; ++i) red[tid >> 6][i] = d[i];
@@ -150,7 +144,7 @@ __global__ __launch_bounds__(1024) void absmean_final_kernel(
         uint64_t sum = 0;
 #pragma unroll
         for (int j = 0; j < 1024 / 64; ++j) sum += col[wv][lane + 64 * j];
-        sum = wave_sum_u64c(sum);
+        sum = wave_sum_u64(sum);
         if (lane == 0) tot[wv] = sum;
     }
     __syncthreads();

@@ -39,23 +39,6 @@ struct FfnShared {
     int more;                     // 1: another window level is needed
 };
 
-// 64-bit lane moves through DPP (two 32-bit moves), for the wave sums below.
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const uint32_t lo = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)dpp_i32<CTRL>((int)(uint32_t)(v >> 32));
-    return (uint64_t)hi << 32 | lo;
-}
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-    v += dpp_u64<kDppXor1>(v);
-    v += dpp_u64<kDppXor2>(v);
-    v += dpp_u64<kDppHalfMirror>(v);
-    v += dpp_u64<kDppMirror>(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
 // Every wave's sum of (a, cnt) into sh.red (as 32-bit digits, each total
 // below 2^42); the caller synchronises before reading them.
 __device__ __forceinline__ void wave_window_sums(const U128 &a, uint32_t cnt, FfnShared &sh) {
@@ -97,8 +80,9 @@ __device__ __forceinline__ double wave_sum_f64(double v) {   // exact here: inte
     add(dpp_u64<kDppXor2>(b));
     add(dpp_u64<kDppHalfMirror>(b));
     add(dpp_u64<kDppMirror>(b));
-    add(__shfl_xor(b, 16, 64));
-    add(__shfl_xor(b, 32, 64));
+    add(dpp_rows_u64<kDppRowBcast15, 0xA>(b));   // the rows a move skips add +0
+    add(dpp_rows_u64<kDppRowBcast31, 0xC>(b));
+    b = readlane63_u64(b);
     double r;
     __builtin_memcpy(&r, &b, 8);
     return r;

@@ -425,8 +425,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelA
         for (int t = 0; t < NT; ++t) {
             if (t < a.ntok) {
                 // a4 and a16 are exact multiples of 4 and 16
+                // the row's sum is complete in its last 16 lanes (group_sum_i32)
                 const int r = group_sum_i32<LPR>(a1[t] + (a4[t] >> 2) + (a16[t] >> 4));
-                if (u == t && row_ok) {
+                if (u == LPR - 1 - t && row_ok) {
                     const int d = r - tsum[t];
                     if (dot) dot[(int64_t)t * M + row] = d;
                     if (y) y[(int64_t)t * M + row] = ((float)d * alpha) / s_tok[t];
