@@ -204,8 +204,11 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
     for (int w = 1; w < kFfnWaves; ++w) hm = fmaxf(hm, sh.redm[w]);
 
     // ---- the exactly rounded sum of h^2 -> the factor c (wave 0 rounds)
+    // Both branches end on a barrier after sh.c is written (hm is the same
+    // in every thread, so the branch is uniform).
     if (hm == 0.0f) {
         if (tid == 0) sh.c = norm_factor(0.0, F, eps);
+        __syncthreads();
     } else {
         uint64_t vmax;
         int Pmax;
@@ -272,7 +275,6 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_act_quant_kernel(
             __syncthreads();
         }
     }
-    __syncthreads();
     const float c = sh.c;
 
     // ---- pass 2: v = (h * c) * gamma in place, and its absmax
