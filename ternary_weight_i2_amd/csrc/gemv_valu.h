@@ -99,12 +99,15 @@ __device__ __forceinline__ int lds_pos(int t, int K, int k) {
 // from clamped, always-valid addresses (a repeated last piece cannot change
 // the absmax and is not emitted); finish() then reduces and quantises.
 // Longer tokens are streamed through twice (absmax pass, quantise pass).
-template <int NT, int MODE, int WAVES>
+template <int NT, int MODE, int WAVES, int XRMAX = 4>
 struct TokenPrologue {
     static constexpr int kThreads = WAVES * 64;
     using V = TokVec<MODE>;
     static constexpr int E = V::kElems;
-    static constexpr int XR = NT == 1 ? 4 : (NT == 2 ? 2 : 1);   // register budget
+    // register budget: at most XRMAX pieces (the most a short-row launch can
+    // need), so no thread issues clamped loads of pieces no launch has
+    static constexpr int XR0 = NT == 1 ? 4 : (NT == 2 ? 2 : 1);
+    static constexpr int XR = XR0 < XRMAX ? XR0 : XRMAX;
     uint4 raw[NT][XR];      // token bits as loaded; widened only in finish()
 
     __device__ static bool fits(const GemvArgs &a) {
@@ -265,6 +268,12 @@ template <int NT, int LPR, int MODE, int JM, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelArgs a) {
     constexpr int kThreads = WAVES * 64;
     constexpr bool kAllChunks = JM <= 4;
+    // token pieces per thread a single-token short-row launch can need
+    // (K <= 64 * JM * LPR); other launches keep the full register budget
+    constexpr int kTokE = MODE == 1 ? 4 : 8;
+    constexpr int kTokXR =
+        (kAllChunks && NT == 1) ? (JM * LPR * 64 / kTokE + WAVES * 64 - 1) / (WAVES * 64) : 4;
+    using Prologue = TokenPrologue<NT, MODE, WAVES, (kTokXR < 1 ? 1 : kTokXR)>;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
     int8_t *xl = reinterpret_cast<int8_t *>(lds);
@@ -363,8 +372,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelA
             sum_tok[tid] = xsum_r;
         }
     } else {
-        TokenPrologue<NT, MODE, WAVES> tp;
-        const bool in_regs = TokenPrologue<NT, MODE, WAVES>::fits(a);
+        Prologue tp;
+        const bool in_regs = Prologue::fits(a);
         if (in_regs) tp.load_tokens(a);
         __builtin_amdgcn_sched_barrier(0);       // keep the token loads ahead of the weights
         load_group(0, cur);
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelA
 #pragma unroll
         for (int t = 0; t < NT; ++t) tsum[t] = sum_tok[t];
     } else {
-        TokenPrologue<NT, MODE, WAVES>::token_sums(a, redi, tsum);
+        Prologue::token_sums(a, redi, tsum);
     }
 
     const int gstride = K >> 2;   // bytes between fields in LDS
