@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 # valid only for the kernel sources with this sha256.
 TRAFFIC = {"sources": ("ternary_weight_i2_amd/csrc/gemv_valu.h", "ternary_weight_i2_amd/csrc/gemv.hip",
                        "ternary_weight_i2_amd/csrc/common.h"),
-           "sha256": "af36b7afb73603e931a01cccd8321c1315b55b979338ef2642474631c90fbf1c",
-           "bytes_per_launch": 4555264}
+           "sha256": "57260f25eb1e0a22878b80bb5c867736de8007d8e1f421c8ab142d8ccaad54ed",
+           "bytes_per_launch": 4552192}
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 # MFMA busy fraction of the prefill GEMM launches (y only), from rocprofv3
 # SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs)
@@ -44,8 +44,8 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, vendor figure
 GEMM_COUNTERS = {"sources": ("ternary_weight_i2_amd/csrc/gemm.hip", "ternary_weight_i2_amd/csrc/gemm_tiles.h",
                              "ternary_weight_i2_amd/csrc/common.h"),
                  "sha256": "d7fb04af8d7923951791ef3388bf461e7a49b5b5766616e45e8210ddc5a14c7b",
-                 "mfma_busy": {4096: {"q/k/v": 0.240, "o": 0.161, "gate/up": 0.287, "down": 0.202},
-                               128: {"q/k/v": 0.015, "o": 0.008, "gate/up": 0.023, "down": 0.011}}}
+                 "mfma_busy": {4096: {"q/k/v": 0.238, "o": 0.157, "gate/up": 0.284, "down": 0.203},
+                               128: {"q/k/v": 0.016, "o": 0.008, "gate/up": 0.024, "down": 0.012}}}
 GROUPS = (("attn", ("q", "k", "v")), ("o", ("o",)), ("ffn", ("gate", "up")),
           ("down", ("down",)))
 

@@ -268,11 +268,11 @@ template <int NT, int LPR, int MODE, int JM, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_valu_kernel(const GemvKernelArgs a) {
     constexpr int kThreads = WAVES * 64;
     constexpr bool kAllChunks = JM <= 4;
-    // token pieces per thread a single-token short-row launch can need
-    // (K <= 64 * JM * LPR); other launches keep the full register budget
+    // token pieces per thread a single-token launch can need (its rows are
+    // at most JM chunks per lane: K <= 64 * JM * LPR); passes of two tokens
+    // keep the full register budget
     constexpr int kTokE = MODE == 1 ? 4 : 8;
-    constexpr int kTokXR =
-        (kAllChunks && NT == 1) ? (JM * LPR * 64 / kTokE + WAVES * 64 - 1) / (WAVES * 64) : 4;
+    constexpr int kTokXR = NT == 1 ? (JM * LPR * 64 / kTokE + WAVES * 64 - 1) / (WAVES * 64) : 4;
     using Prologue = TokenPrologue<NT, MODE, WAVES, (kTokXR < 1 ? 1 : kTokXR)>;
     constexpr int RG = 64 / LPR;            // rows per wave per row group
     extern __shared__ int4 lds[];
